@@ -1,0 +1,32 @@
+"""Helpers shared by the GPU parity tests."""
+import sys
+
+import numpy as np
+import torch
+
+from token_level_sparse_lightning_amd import synth
+
+DEV = "cuda:0"
+
+
+def announce(msg: str):
+    """Name the case before a GPU step (so a failing run says which one)."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x):
+    return None if x is None else x.to(DEV, non_blocking=False).contiguous()
+
+
+def host(x):
+    return synth.storage_to_numpy(x)
+
+
+def sample_rows(n, k, count, seed=0, extra=()):
+    """Query rows to check against the oracle: edges around k and n, plus random."""
+    base = {0, 1, min(n - 1, k - 2), min(n - 1, k - 1), min(n - 1, k), min(n - 1, k + 1), n - 1, n - 2}
+    base |= {int(e) for e in extra if 0 <= e < n}
+    rng = np.random.default_rng(seed)
+    rest = rng.choice(n, size=min(n, count), replace=False)
+    return np.array(sorted({int(x) for x in base if x >= 0} | {int(x) for x in rest}), dtype=np.int64)

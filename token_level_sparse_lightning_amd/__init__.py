@@ -1,0 +1,19 @@
+"""DSA token-level sparse selection for AMD Instinct MI355X (gfx950).
+
+The compute lives in libtlsl.so (hand-written HIP kernels behind the C ABI of
+``include/tlsl.h``); this package only loads it and marshals torch tensors.
+"""
+from .binding import (  # noqa: F401
+    BF16,
+    F32,
+    FP8_E4M3,
+    TlslError,
+    index_decode,
+    index_prefill,
+    index_prefill_workspace_bytes,
+    load,
+    sparse_attn_decode,
+    sparse_attn_decode_workspace_bytes,
+    sparse_attn_prefill,
+    topk_select,
+)

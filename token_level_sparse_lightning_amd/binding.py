@@ -1,0 +1,198 @@
+"""ctypes binding of libtlsl.so (the C ABI in include/tlsl.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream, every step of the computation runs in the library's kernels.  There
+is no CPU path: if the library is missing the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtlsl.so")
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+
+EXPORTS = ("index_prefill", "index_decode", "topk_select", "sparse_attn_prefill",
+           "sparse_attn_decode", "tlsl_last_error", "tlsl_version")
+
+_lib = None
+
+
+class TlslError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed ({code}): {msg}")
+        self.code = code
+
+
+def load():
+    """Load libtlsl.so (built by ``token_level_sparse_lightning_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m token_level_sparse_lightning_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)
+    F = ctypes.c_float
+    lib.index_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, P, SZ, P]
+    lib.index_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, SZ, P]
+    lib.topk_select.argtypes = [P, P, P, I, I, I, P, P, P, SZ, P]
+    lib.sparse_attn_prefill.argtypes = [P, P, P, I, I, I, I, I, I, F, I, P, P, P, SZ, P]
+    lib.sparse_attn_decode.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, P, P, SZ, P]
+    for fn in ("index_prefill", "index_decode", "topk_select", "sparse_attn_prefill", "sparse_attn_decode"):
+        getattr(lib, fn).restype = I
+    lib.tlsl_last_error.restype = ctypes.c_char_p
+    lib.tlsl_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise TlslError(fn, rc, _lib.tlsl_last_error().decode())
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _need(t, name):
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+# ---------------------------------------------------------------------------
+def index_prefill_workspace_bytes(qI, kI, wI, k, q_scale=None, k_scale=None) -> int:
+    lib = load()
+    B, n, HI, DI = qI.shape
+    size = ctypes.c_size_t(0)
+    dummy = ctypes.c_void_p(16)  # never dereferenced by a size query
+    rc = lib.index_prefill(dummy, dummy if q_scale is not None else None, dummy,
+                           dummy if k_scale is not None else None, dummy, B, n, HI, DI, k,
+                           dtype_code(qI), dummy, None, None, ctypes.byref(size), None)
+    _check("index_prefill", rc)
+    return size.value
+
+
+def index_prefill(qI, kI, wI, k, q_scale=None, k_scale=None, S=None, S_score=None,
+                  want_scores=False, workspace=None, stream=None):
+    """Lightning Indexer + causal top-k: returns (S [B,n,k] int32, S_score or None)."""
+    lib = load()
+    for t, nm in ((qI, "qI"), (kI, "kI"), (wI, "wI"), (q_scale, "q_scale"), (k_scale, "k_scale")):
+        _need(t, nm)
+    B, n, HI, DI = qI.shape
+    if S is None:
+        S = torch.empty((B, n, k), dtype=torch.int32, device=qI.device)
+    if S_score is None and want_scores:
+        S_score = torch.empty((B, n, k), dtype=torch.float32, device=qI.device)
+    if workspace is None:
+        workspace = torch.empty(index_prefill_workspace_bytes(qI, kI, wI, k, q_scale, k_scale),
+                                dtype=torch.uint8, device=qI.device)
+    size = ctypes.c_size_t(workspace.numel())
+    rc = lib.index_prefill(_ptr(qI), _ptr(q_scale), _ptr(kI), _ptr(k_scale), _ptr(wI), B, n, HI,
+                           DI, k, dtype_code(qI), _ptr(S), _ptr(S_score), _ptr(workspace),
+                           ctypes.byref(size), _stream(stream))
+    _check("index_prefill", rc)
+    return S, S_score
+
+
+def index_decode(qI, kI_cache, wI, cu_seqlens, max_len, q_scale=None, k_scale=None,
+                 scores=None, stream=None):
+    """Decode indexer scan: returns scores [sumL] fp32, packed like the cache."""
+    lib = load()
+    B, HI, DI = qI.shape
+    total = kI_cache.shape[0]
+    if scores is None:
+        scores = torch.empty(total, dtype=torch.float32, device=qI.device)
+    rc = lib.index_decode(_ptr(qI), _ptr(q_scale), _ptr(kI_cache), _ptr(k_scale), _ptr(wI),
+                          _ptr(cu_seqlens), B, HI, DI, int(max_len), dtype_code(qI), _ptr(scores),
+                          None, None, _stream(stream))
+    _check("index_decode", rc)
+    return scores
+
+
+def topk_select(scores, row_start, row_len, k, max_len, S=None, S_score=None, want_scores=False,
+                stream=None):
+    """Row top-k: returns (S [R,k] int32 row-relative, S_score or None)."""
+    lib = load()
+    R = row_len.shape[0]
+    if S is None:
+        S = torch.empty((R, k), dtype=torch.int32, device=scores.device)
+    if S_score is None and want_scores:
+        S_score = torch.empty((R, k), dtype=torch.float32, device=scores.device)
+    rc = lib.topk_select(_ptr(scores), _ptr(row_start), _ptr(row_len), R, k, int(max_len), _ptr(S),
+                         _ptr(S_score), None, None, _stream(stream))
+    _check("topk_select", rc)
+    return S, S_score
+
+
+def sparse_attn_prefill(q, kv, S, softmax_scale, Dv, out=None, lse=None, want_lse=False,
+                        stream=None):
+    """Sparse attention for a prefill batch: returns (out [B,n,H,Dv], lse or None)."""
+    lib = load()
+    B, n, H, Dqk = q.shape
+    k = S.shape[-1]
+    if out is None:
+        out = torch.empty((B, n, H, Dv), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, n, H), dtype=torch.float32, device=q.device)
+    rc = lib.sparse_attn_prefill(_ptr(q), _ptr(kv), _ptr(S), B, n, H, Dqk, Dv, k,
+                                 float(softmax_scale), dtype_code(q), _ptr(out), _ptr(lse), None,
+                                 None, _stream(stream))
+    _check("sparse_attn_prefill", rc)
+    return out, lse
+
+
+def sparse_attn_decode_workspace_bytes(q, kv_cache, S, Dv) -> int:
+    lib = load()
+    B, H, Dqk = q.shape
+    size = ctypes.c_size_t(0)
+    dummy = ctypes.c_void_p(16)
+    rc = lib.sparse_attn_decode(dummy, dummy, dummy, dummy, B, H, Dqk, Dv, S.shape[-1], 1.0,
+                                dtype_code(q), dummy, None, None, ctypes.byref(size), None)
+    _check("sparse_attn_decode", rc)
+    return size.value
+
+
+def sparse_attn_decode(q, kv_cache, cu_seqlens, S, softmax_scale, Dv, out=None, lse=None,
+                       want_lse=False, workspace=None, stream=None):
+    """Sparse attention for the newest token of each sequence: (out [B,H,Dv], lse or None)."""
+    lib = load()
+    B, H, Dqk = q.shape
+    k = S.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(sparse_attn_decode_workspace_bytes(q, kv_cache, S, Dv),
+                                dtype=torch.uint8, device=q.device)
+    size = ctypes.c_size_t(workspace.numel())
+    rc = lib.sparse_attn_decode(_ptr(q), _ptr(kv_cache), _ptr(cu_seqlens), _ptr(S), B, H, Dqk, Dv,
+                                k, float(softmax_scale), dtype_code(q), _ptr(out), _ptr(lse),
+                                _ptr(workspace), ctypes.byref(size), _stream(stream))
+    _check("sparse_attn_decode", rc)
+    return out, lse

@@ -1,0 +1,681 @@
+// indexer.hip -- Lightning Indexer scoring and causal top-k on gfx950.
+//
+// The score of the DSA page, section 1.1 eq.(1), is a contraction over the
+// indexer dimension followed by ReLU and a weighted sum over the indexer heads.
+// It runs on the matrix cores as a 16x16 tile per (16 heads x 16 keys) block:
+// heads on the M side, keys on the N side, dI on the reduction side.  ReLU, the
+// weights and the head sum stay in registers (the epilogue), so no score
+// matrix is stored.
+//
+// Prefill (eq.(2) for every row of a B x n batch) runs in three stages:
+//  1. prefill_score: a workgroup owns 8*QW consecutive queries.  It first
+//     scores them against every STRIDE-th key ("sample pass") and takes, per
+//     query, a high order statistic of the sample as a conservative score
+//     threshold.  It then walks all causal key tiles from the diagonal down,
+//     appends every (score, position) that reaches the threshold to the
+//     query's candidate buffer (descending position order) and counts them.
+//  2. prefill_finalize: one workgroup per row selects the exact top-k from the
+//     buffer (radix select in LDS) and writes S in ascending position order.
+//     A row whose buffer missed (fewer candidates than min(k, t+1): the sample
+//     threshold overshot) or overflowed goes on a fallback list.
+//  3. prefill_fallback: rescores each listed row in full and selects from it.
+// The result does not depend on the threshold: every key that can be in the
+// top-k reaches the buffer, or the row is recomputed.
+//
+// Decode (index_decode) scores the newest query of each sequence against its
+// whole packed key cache with the same tile code, so a decode row equals the
+// prefill row at the same length bit for bit.
+#include <math.h>
+
+#include "tlsl_device.h"
+#include "tlsl_internal.h"
+#include "topk_common.h"
+
+namespace tlsl {
+
+// ---------------------------------------------------------------------------
+// Scoring tile shared by every indexer kernel.
+// ---------------------------------------------------------------------------
+template <int DT, int HB, int DI>
+struct Idx {
+    using M = Mma<DT, DI>;
+    static constexpr int NCH = M::NCH;
+    static constexpr int ROWB = M::ROWB;
+
+    // Query fragment of one token (HB blocks of 16 heads) and the lane's head
+    // weights (rows 4g..4g+3 of each block), pre-multiplied by the token scale.
+    __device__ __forceinline__ static void load_query(const unsigned char* q_tok, const float* w_tok,
+                                                      float wmul, int HI, bool valid,
+                                                      uint4 (&qf)[HB][NCH], float (&wv)[HB][4]) {
+        const int l = lane_id(), g = l >> 4, c = l & 15;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            const int h = 16 * hb + c;
+            const bool ok = valid && h < HI;
+            const uint4* src = reinterpret_cast<const uint4*>(q_tok + (size_t)(ok ? h : 0) * ROWB + g * (ROWB / 4));
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) qf[hb][ch] = ok ? src[ch] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int hh = 16 * hb + 4 * g + r;
+                wv[hb][r] = (valid && hh < HI) ? w_tok[hh] * wmul : 0.f;
+            }
+        }
+    }
+
+    // Scores of one query against a 64-key subtile whose key fragments are
+    // kf[kb] (keys 16*kb + (l & 15)).  Lane l receives key l's score (before
+    // the key scale).
+    __device__ __forceinline__ static float score(const uint4 (&qf)[HB][NCH], const float (&wv)[HB][4],
+                                                  const uint4 (&kf)[4][NCH]) {
+        float part[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            v4f acc[HB];
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) acc[hb] = M::run(qf[hb], kf[kb], v4f{0.f, 0.f, 0.f, 0.f});
+            float p = 0.f;
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) p = __builtin_fmaf(wv[hb][r], fmaxf(acc[hb][r], 0.f), p);
+            part[kb] = p;
+        }
+        return reduce_heads_64(part);
+    }
+
+    // Key fragments of keys key0 + 16*kb + (l & 15), rows clamped to last,
+    // straight from global memory.
+    __device__ __forceinline__ static void load_keys_global(const unsigned char* kbase, int key0, int last,
+                                                            uint4 (&kf)[4][NCH]) {
+        const int l = lane_id(), g = l >> 4, c = l & 15;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int key = min(key0 + 16 * kb + c, last);
+            const uint4* src = reinterpret_cast<const uint4*>(kbase + (size_t)key * ROWB + g * (ROWB / 4));
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) kf[kb][ch] = src[ch];
+        }
+    }
+};
+
+// LDS image of a 64-key subtile: rows padded by 16 bytes so that the 16 lanes
+// of a lane group read 16 different rows without bank conflicts.
+template <int DT, int DI>
+struct KTile {
+    static constexpr int ROWB = DI * ElemBytes<DT>::v;
+    static constexpr int STRIDE = ROWB + 16;
+    static constexpr int BYTES = 64 * STRIDE;
+    static constexpr int CPR = ROWB / 16;       // 16-B chunks per row
+    static constexpr int CHUNKS = 64 * CPR;     // per subtile
+};
+
+constexpr int PF_WAVES = 8;
+constexpr int PF_NT = PF_WAVES * 64;
+constexpr int PF_RBUF = 512;      // per-query LDS buffer of sample scores
+constexpr float PF_SIGMA = 4.0f;  // safety margin of the sample threshold, in standard deviations
+
+struct PrefillArgs {
+    const unsigned char* q;
+    const float* q_scale;
+    const unsigned char* k;
+    const float* k_scale;
+    const float* w;
+    int B, n, HI, topk, cap, stride, tiles;
+    uint2* buf;      // [B*n][cap] (score bits, position)
+    int* cnt;        // [B*n] candidates found (may exceed cap)
+    int* fb_count;   // fallback list length (zeroed here)
+};
+
+// r-th largest value (1-based) of vals[0..cnt) in LDS, owned by one wave, and
+// the count of values strictly above it.
+__device__ float wave_kth_largest(const float* vals, int cnt, int r, uint32_t* hist, int* gt_out) {
+    const int l = lane_id();
+    uint32_t prefix = 0, pmask = 0;
+    int need = r, gt = 0;
+    for (int sh = 24; sh >= 0; sh -= 8) {
+        for (int i = l; i < 256; i += 64) hist[i] = 0;
+        wave_lds_fence();
+        for (int i = l; i < cnt; i += 64) {
+            const uint32_t key = score_key(vals[i]);
+            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & 255u], 1u);
+        }
+        wave_lds_fence();
+        int above;
+        const int d = wave_find_bin<256>(hist, need, &above);
+        gt += above;
+        need -= above;
+        prefix |= (uint32_t)d << sh;
+        pmask |= 255u << sh;
+        wave_lds_fence();
+    }
+    *gt_out = gt;
+    return key_score(prefix);
+}
+
+// Number of sample values the threshold keeps for query t: the expected count
+// of sample keys inside the final top-K plus PF_SIGMA standard deviations.
+// Returns 0 when no useful threshold exists.
+__device__ __forceinline__ int sample_rank(int t, int topk, int stride) {
+    const int ns = t / stride + 1;
+    const int K = min(topk, t + 1);
+    const float mu = (float)ns * (float)K / (float)(t + 1);
+    const int r = (int)ceilf(mu + PF_SIGMA * sqrtf(mu)) + 2;
+    return (r < ns && r <= PF_RBUF - 64) ? r : 0;
+}
+
+template <int DT, int HB, int DI, int QW>
+__global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) {
+    using I = Idx<DT, HB, DI>;
+    using KT = KTile<DT, DI>;
+    constexpr int NCH = I::NCH;
+    constexpr int TQ = PF_WAVES * QW;
+    __shared__ __align__(16) unsigned char ktile[2][KT::BYTES];
+    __shared__ float rbuf[TQ][PF_RBUF];
+    __shared__ uint32_t whist[PF_WAVES][256];
+
+    const int tid = threadIdx.x, wv_id = tid >> 6, l = lane_id(), g = l >> 4, c = l & 15;
+    const int b = blockIdx.x % a.B;
+    const int tile = a.tiles - 1 - blockIdx.x / a.B;  // heaviest tiles first
+    const int t0 = tile * TQ;
+    const int t_last = min(t0 + TQ, a.n) - 1;
+    if (blockIdx.x == 0 && tid == 0) *a.fb_count = 0;
+
+    const size_t tok0 = (size_t)b * a.n;
+    const unsigned char* kb_base = a.k + tok0 * KT::ROWB;
+
+    int tq[QW];
+    bool qv[QW];
+    uint4 qf[QW][HB][NCH];
+    float wv[QW][HB][4];
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+        tq[i] = t0 + wv_id * QW + i;
+        qv[i] = tq[i] < a.n;
+        const size_t row = tok0 + (qv[i] ? tq[i] : 0);
+        const float wmul = (DT == kFP8) ? a.q_scale[row] : 1.f;
+        I::load_query(a.q + row * (size_t)a.HI * KT::ROWB, a.w + row * a.HI, wmul, a.HI, qv[i], qf[i], wv[i]);
+    }
+
+    // cooperative copy of 64 key rows (row r <- key key_of(r), clamped) into LDS
+    auto copy_rows = [&](unsigned char* dst, int key0, int kstep) {
+        for (int ch = tid; ch < KT::CHUNKS; ch += PF_NT) {
+            const int r = ch / KT::CPR, off = (ch % KT::CPR) * 16;
+            const int key = min(key0 + r * kstep, a.n - 1);
+            *reinterpret_cast<uint4*>(dst + r * KT::STRIDE + off) =
+                *reinterpret_cast<const uint4*>(kb_base + (size_t)key * KT::ROWB + off);
+        }
+    };
+    auto frag_from_lds = [&](const unsigned char* src, uint4 (&kf)[4][NCH]) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const uint4* p = reinterpret_cast<const uint4*>(src + (16 * kb + c) * KT::STRIDE + g * (KT::ROWB / 4));
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) kf[kb][ch] = p[ch];
+        }
+    };
+
+    // ---- sample pass: conservative per-query threshold ----------------------
+    float theta[QW];
+    int rneed[QW];
+    bool any_pre = false;
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+        theta[i] = -INFINITY;
+        rneed[i] = (qv[i] && tq[i] + 1 > a.cap) ? sample_rank(tq[i], a.topk, a.stride) : 0;
+        any_pre |= rneed[i] > 0;
+    }
+    if (__syncthreads_or(any_pre)) {
+        int rc[QW];
+        float rth[QW];
+#pragma unroll
+        for (int i = 0; i < QW; ++i) { rc[i] = 0; rth[i] = -INFINITY; }
+        const int nsamp = t_last / a.stride + 1;
+        for (int js = 0; js * 64 < nsamp; ++js) {
+            __syncthreads();
+            copy_rows(ktile[0], js * 64 * a.stride, a.stride);
+            __syncthreads();
+            uint4 kf[4][NCH];
+            frag_from_lds(ktile[0], kf);
+            const int s = (js * 64 + l) * a.stride;
+            const float ks = (DT == kFP8) ? a.k_scale[tok0 + min(s, a.n - 1)] : 1.f;
+#pragma unroll
+            for (int i = 0; i < QW; ++i) {
+                if (rneed[i] == 0 || js * 64 * a.stride > tq[i]) continue;
+                float sc = I::score(qf[i], wv[i], kf);
+                if (DT == kFP8) sc *= ks;
+                const bool ok = s <= tq[i] && sc >= rth[i];
+                const uint64_t m = ballot(ok);
+                float* rb = rbuf[wv_id * QW + i];
+                if (ok) rb[rc[i] + rank_below(m)] = sc;
+                rc[i] += __popcll(m);
+                if (rc[i] > PF_RBUF - 64) {
+                    // keep the rneed largest values, raise the sample threshold
+                    wave_lds_fence();
+                    int gt;
+                    const float v = wave_kth_largest(rb, rc[i], rneed[i], whist[wv_id], &gt);
+                    float vals[PF_RBUF / 64];
+#pragma unroll
+                    for (int j = 0; j < PF_RBUF / 64; ++j) vals[j] = (l + 64 * j < rc[i]) ? rb[l + 64 * j] : -INFINITY;
+                    wave_lds_fence();
+                    int outc = 0;
+#pragma unroll
+                    for (int j = 0; j < PF_RBUF / 64; ++j) {
+                        const bool keep = (l + 64 * j < rc[i]) && vals[j] > v;
+                        const uint64_t mk = ballot(keep);
+                        if (keep) rb[outc + rank_below(mk)] = vals[j];
+                        outc += __popcll(mk);
+                    }
+                    for (int j = outc + l; j < rneed[i]; j += 64) rb[j] = v;
+                    wave_lds_fence();
+                    rc[i] = rneed[i];
+                    rth[i] = v;
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < QW; ++i) {
+            if (rneed[i] > 0 && rc[i] >= rneed[i]) {
+                wave_lds_fence();
+                int gt;
+                theta[i] = wave_kth_largest(rbuf[wv_id * QW + i], rc[i], rneed[i], whist[wv_id], &gt);
+            }
+        }
+    }
+
+    // ---- main pass: every causal key, diagonal first -----------------------
+    int cntq[QW];
+#pragma unroll
+    for (int i = 0; i < QW; ++i) cntq[i] = 0;
+    const int nsub = t_last / 64 + 1;
+    __syncthreads();
+    copy_rows(ktile[0], (nsub - 1) * 64, 1);
+    __syncthreads();
+    for (int it = 0; it < nsub; ++it) {
+        const int j = nsub - 1 - it;
+        const int cur = it & 1;
+        // prefetch the next subtile into registers
+        constexpr int PER = (KT::CHUNKS + PF_NT - 1) / PF_NT;
+        uint4 pre[PER];
+        if (j > 0) {
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int ch = tid + u * PF_NT;
+                if (ch < KT::CHUNKS) {
+                    const int r = ch / KT::CPR, off = (ch % KT::CPR) * 16;
+                    pre[u] = *reinterpret_cast<const uint4*>(kb_base + (size_t)((j - 1) * 64 + r) * KT::ROWB + off);
+                }
+            }
+        }
+        uint4 kf[4][NCH];
+        frag_from_lds(ktile[cur], kf);
+        const int s = j * 64 + l;
+        const float ks = (DT == kFP8) ? a.k_scale[tok0 + min(s, a.n - 1)] : 1.f;
+#pragma unroll
+        for (int i = 0; i < QW; ++i) {
+            if (!qv[i] || j * 64 > tq[i]) continue;
+            float sc = I::score(qf[i], wv[i], kf);
+            if (DT == kFP8) sc *= ks;
+            const bool ok = s <= tq[i] && sc >= theta[i];
+            const uint64_t m = ballot(ok);
+            const int slot = cntq[i] + rank_above(m);
+            if (ok && slot < a.cap)
+                a.buf[(tok0 + tq[i]) * (size_t)a.cap + slot] = make_uint2(__float_as_uint(sc), (uint32_t)s);
+            cntq[i] += __popcll(m);
+        }
+        if (j > 0) {
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int ch = tid + u * PF_NT;
+                if (ch < KT::CHUNKS) {
+                    const int r = ch / KT::CPR, off = (ch % KT::CPR) * 16;
+                    *reinterpret_cast<uint4*>(ktile[cur ^ 1] + r * KT::STRIDE + off) = pre[u];
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (l == 0) {
+#pragma unroll
+        for (int i = 0; i < QW; ++i)
+            if (qv[i]) a.cnt[tok0 + tq[i]] = cntq[i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2: exact selection from a row's candidate buffer.
+// ---------------------------------------------------------------------------
+constexpr int FIN_NT = 256;
+
+struct FinalizeArgs {
+    const uint2* buf;
+    const int* cnt;
+    int n, topk, cap;
+    int32_t* S;
+    float* Ss;
+    int* fb_count;
+    int* fb_list;
+};
+
+template <int CAPMAX>
+__global__ __launch_bounds__(FIN_NT) void prefill_finalize_kernel(FinalizeArgs a) {
+    __shared__ float fsc[CAPMAX];
+    __shared__ int fpos[CAPMAX];
+    __shared__ uint32_t hist[2048];
+    __shared__ int scratch[64];
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x;
+    const int t = row % a.n;
+    const int K = min(a.topk, t + 1);
+    const int cnt = a.cnt[row];
+    if (cnt < K || cnt > a.cap) {
+        if (tid == 0) a.fb_list[atomicAdd(a.fb_count, 1)] = row;
+        return;
+    }
+    const uint2* src = a.buf + (size_t)row * a.cap;
+    for (int i = tid; i < cnt; i += FIN_NT) {
+        const uint2 e = src[i];
+        fsc[cnt - 1 - i] = __uint_as_float(e.x);  // ascending position order
+        fpos[cnt - 1 - i] = (int)e.y;
+    }
+    __syncthreads();
+    uint32_t T = 0u;
+    int gt = cnt;
+    if (cnt > K) {
+        uint32_t prefix = 0, pmask = 0;
+        int need = K;
+        gt = 0;
+        for (int p = 0; p < 3; ++p) {
+            const int sh = radix_shift(p);
+            const uint32_t dm = radix_mask(p);
+            for (int i = tid; i < 2048; i += FIN_NT) hist[i] = 0;
+            __syncthreads();
+            for (int i = tid; i < cnt; i += FIN_NT) {
+                const uint32_t key = score_key(fsc[i]);
+                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
+            }
+            __syncthreads();
+            int above;
+            const int d = block_find_bin<FIN_NT, 2048>(hist, need, &above, scratch);
+            gt += above;
+            need -= above;
+            prefix |= (uint32_t)d << sh;
+            pmask |= dm << sh;
+        }
+        T = prefix;
+    }
+    const int need_ties = K - gt;
+    int32_t* Srow = a.S + (size_t)row * a.topk;
+    float* Ssrow = a.Ss ? a.Ss + (size_t)row * a.topk : nullptr;
+    int run_sel = 0, run_tie = 0;
+    for (int base = 0; base < cnt && run_sel < K; base += FIN_NT) {
+        const int i = base + tid;
+        const bool v = i < cnt;
+        const float s = v ? fsc[i] : 0.f;
+        const uint32_t key = v ? score_key(s) : 0u;
+        const bool isgt = v && key > T, istie = v && key == T;
+        int rt, rdum, tt, tdum;
+        block_scan2<FIN_NT>(istie, false, &rt, &rdum, &tt, &tdum, scratch);
+        const bool sel = isgt || (istie && run_tie + rt < need_ties);
+        int rs, ts;
+        block_scan2<FIN_NT>(sel, false, &rs, &rdum, &ts, &tdum, scratch);
+        if (sel) {
+            Srow[run_sel + rs] = fpos[i];
+            if (Ssrow) Ssrow[run_sel + rs] = s;
+        }
+        run_sel += ts;
+        run_tie += tt;
+    }
+    for (int i = K + tid; i < a.topk; i += FIN_NT) {
+        Srow[i] = -1;
+        if (Ssrow) Ssrow[i] = -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 3: rows whose buffer missed or overflowed are rescored in full.
+// ---------------------------------------------------------------------------
+constexpr int FB_NT = 512;
+
+struct FallbackArgs {
+    const unsigned char* q;
+    const float* q_scale;
+    const unsigned char* k;
+    const float* k_scale;
+    const float* w;
+    int n, HI, topk;
+    const int* fb_count;
+    const int* fb_list;
+    float* scratch;  // [gridDim.x][n]
+    int32_t* S;
+    float* Ss;
+};
+
+template <int DT, int HB, int DI>
+__global__ __launch_bounds__(FB_NT) void prefill_fallback_kernel(FallbackArgs a) {
+    using I = Idx<DT, HB, DI>;
+    constexpr int NCH = I::NCH;
+    __shared__ TopkSmem sm;
+    const int nfb = *a.fb_count;
+    const int w = threadIdx.x >> 6, l = lane_id();
+    float* sc = a.scratch + (size_t)blockIdx.x * a.n;
+    for (int it = blockIdx.x; it < nfb; it += gridDim.x) {
+        const int row = a.fb_list[it];
+        const int t = row % a.n;
+        const size_t tok0 = (size_t)row - t;
+        uint4 qf[HB][NCH];
+        float wv[HB][4];
+        const float wmul = (DT == kFP8) ? a.q_scale[row] : 1.f;
+        I::load_query(a.q + (size_t)row * a.HI * I::ROWB, a.w + (size_t)row * a.HI, wmul, a.HI, true, qf, wv);
+        const unsigned char* kb_base = a.k + tok0 * I::ROWB;
+        for (int j = w; j * 64 <= t; j += FB_NT / 64) {
+            uint4 kf[4][NCH];
+            I::load_keys_global(kb_base, j * 64, t, kf);
+            float s = I::score(qf, wv, kf);
+            const int key = j * 64 + l;
+            if (DT == kFP8) s *= a.k_scale[tok0 + min(key, t)];
+            if (key <= t) sc[key] = s;
+        }
+        __threadfence();
+        __syncthreads();
+        __threadfence();
+        block_topk_row<FB_NT>(sc, t + 1, a.topk, a.S + (size_t)row * a.topk,
+                              a.Ss ? a.Ss + (size_t)row * a.topk : nullptr, sm);
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode scan: one query per sequence against its packed key cache.
+// ---------------------------------------------------------------------------
+constexpr int DEC_NT = 256;
+constexpr int DEC_CHUNK = 2048;  // keys per workgroup
+
+template <int DT, int HB, int DI>
+__global__ __launch_bounds__(DEC_NT) void decode_score_kernel(const unsigned char* q, const float* q_scale,
+                                                              const unsigned char* kc, const float* k_scale,
+                                                              const float* w, const int64_t* cu, int HI,
+                                                              float* scores) {
+    using I = Idx<DT, HB, DI>;
+    constexpr int NCH = I::NCH;
+    const int b = blockIdx.y;
+    const int64_t start = cu[b];
+    const int L = (int)(cu[b + 1] - start);
+    const int base = blockIdx.x * DEC_CHUNK;
+    if (base >= L) return;
+    const int wv_id = threadIdx.x >> 6, l = lane_id();
+    uint4 qf[HB][NCH];
+    float wv[HB][4];
+    const float wmul = (DT == kFP8) ? q_scale[b] : 1.f;
+    I::load_query(q + (size_t)b * HI * I::ROWB, w + (size_t)b * HI, wmul, HI, true, qf, wv);
+    const unsigned char* kb_base = kc + (size_t)start * I::ROWB;
+    const int end = min(L, base + DEC_CHUNK);
+    for (int j0 = base + 64 * wv_id; j0 < end; j0 += 64 * (DEC_NT / 64)) {
+        uint4 kf[4][NCH];
+        I::load_keys_global(kb_base, j0, L - 1, kf);
+        float s = I::score(qf, wv, kf);
+        const int key = j0 + l;
+        if (DT == kFP8) s *= k_scale[start + min(key, L - 1)];
+        if (key < L) scores[start + key] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers.
+// ---------------------------------------------------------------------------
+bool indexer_supported(const IndexerShape& s) {
+    if (s.HI < 1 || s.HI > 64) return false;
+    if (s.dt == kFP8) return s.DI == 128;
+    if (s.dt == kBF16) return s.DI == 32 || s.DI == 64 || s.DI == 128;
+    if (s.dt == kF32) return s.DI == 32 || s.DI == 64;
+    return false;
+}
+
+static int head_blocks(int HI) { return HI <= 16 ? 1 : (HI <= 32 ? 2 : 4); }
+static int queries_per_wave(const IndexerShape& s) {
+    const int eb = s.dt == kF32 ? 4 : (s.dt == kBF16 ? 2 : 1);
+    const int nch = s.DI * eb / 64;
+    return nch * head_blocks(s.HI) <= 8 ? 2 : 1;
+}
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+PrefillPlan plan_prefill(const IndexerShape& s, int B, int n, int k) {
+    PrefillPlan p{};
+    p.cap = (int)((2 * (size_t)k + 256 + 255) / 256 * 256);
+    p.stride = k >= 2048 ? 16 : (k >= 128 ? k / 128 : 1);
+    p.fb_blocks = 128;
+    const size_t rows = (size_t)B * n;
+    size_t off = 0;
+    p.off_buf = off;
+    off = align256(off + rows * p.cap * sizeof(uint2));
+    p.off_cnt = off;
+    off = align256(off + rows * sizeof(int));
+    p.off_fbcount = off;
+    off = align256(off + sizeof(int));
+    p.off_fblist = off;
+    off = align256(off + rows * sizeof(int));
+    p.off_fbscratch = off;
+    off = align256(off + (size_t)p.fb_blocks * n * sizeof(float));
+    p.ws_bytes = off;
+    (void)s;
+    return p;
+}
+
+template <int DT, int HB, int DI>
+static hipError_t launch_prefill_t(const PrefillArgs& pa, const FinalizeArgs& fa, const FallbackArgs& fb,
+                                   int qw, int rows, int cap, int fb_blocks, hipStream_t st) {
+    if (qw == 2)
+        hipLaunchKernelGGL((prefill_score_kernel<DT, HB, DI, 2>), dim3(pa.tiles * pa.B), dim3(PF_NT), 0, st, pa);
+    else
+        hipLaunchKernelGGL((prefill_score_kernel<DT, HB, DI, 1>), dim3(pa.tiles * pa.B), dim3(PF_NT), 0, st, pa);
+    if (cap <= 1024)
+        hipLaunchKernelGGL((prefill_finalize_kernel<1024>), dim3(rows), dim3(FIN_NT), 0, st, fa);
+    else if (cap <= 4352)
+        hipLaunchKernelGGL((prefill_finalize_kernel<4352>), dim3(rows), dim3(FIN_NT), 0, st, fa);
+    else
+        hipLaunchKernelGGL((prefill_finalize_kernel<8448>), dim3(rows), dim3(FIN_NT), 0, st, fa);
+    hipLaunchKernelGGL((prefill_fallback_kernel<DT, HB, DI>), dim3(fb_blocks), dim3(FB_NT), 0, st, fb);
+    return hipGetLastError();
+}
+
+template <int DT, int DI>
+static hipError_t launch_prefill_hb(int hb, const PrefillArgs& pa, const FinalizeArgs& fa, const FallbackArgs& fb,
+                                    int qw, int rows, int cap, int fbb, hipStream_t st) {
+    if (hb == 1) return launch_prefill_t<DT, 1, DI>(pa, fa, fb, qw, rows, cap, fbb, st);
+    if (hb == 2) return launch_prefill_t<DT, 2, DI>(pa, fa, fb, qw, rows, cap, fbb, st);
+    return launch_prefill_t<DT, 4, DI>(pa, fa, fb, qw, rows, cap, fbb, st);
+}
+
+hipError_t launch_index_prefill(const IndexerShape& s, const void* q, const float* q_scale, const void* k,
+                                const float* k_scale, const float* w, int B, int n, int topk, int32_t* S,
+                                float* S_score, void* ws, const PrefillPlan& plan, hipStream_t st) {
+    unsigned char* wsb = static_cast<unsigned char*>(ws);
+    const int qw = queries_per_wave(s);
+    const int tq = PF_WAVES * qw;
+    PrefillArgs pa;
+    pa.q = static_cast<const unsigned char*>(q);
+    pa.q_scale = q_scale;
+    pa.k = static_cast<const unsigned char*>(k);
+    pa.k_scale = k_scale;
+    pa.w = w;
+    pa.B = B;
+    pa.n = n;
+    pa.HI = s.HI;
+    pa.topk = topk;
+    pa.cap = plan.cap;
+    pa.stride = plan.stride;
+    pa.tiles = (n + tq - 1) / tq;
+    pa.buf = reinterpret_cast<uint2*>(wsb + plan.off_buf);
+    pa.cnt = reinterpret_cast<int*>(wsb + plan.off_cnt);
+    pa.fb_count = reinterpret_cast<int*>(wsb + plan.off_fbcount);
+    FinalizeArgs fa;
+    fa.buf = pa.buf;
+    fa.cnt = pa.cnt;
+    fa.n = n;
+    fa.topk = topk;
+    fa.cap = plan.cap;
+    fa.S = S;
+    fa.Ss = S_score;
+    fa.fb_count = pa.fb_count;
+    fa.fb_list = reinterpret_cast<int*>(wsb + plan.off_fblist);
+    FallbackArgs fb;
+    fb.q = pa.q;
+    fb.q_scale = q_scale;
+    fb.k = pa.k;
+    fb.k_scale = k_scale;
+    fb.w = w;
+    fb.n = n;
+    fb.HI = s.HI;
+    fb.topk = topk;
+    fb.fb_count = pa.fb_count;
+    fb.fb_list = fa.fb_list;
+    fb.scratch = reinterpret_cast<float*>(wsb + plan.off_fbscratch);
+    fb.S = S;
+    fb.Ss = S_score;
+    const int hb = head_blocks(s.HI);
+    const int rows = B * n;
+    if (s.dt == kFP8) return launch_prefill_hb<kFP8, 128>(hb, pa, fa, fb, qw, rows, plan.cap, plan.fb_blocks, st);
+    if (s.dt == kBF16) {
+        if (s.DI == 32) return launch_prefill_hb<kBF16, 32>(hb, pa, fa, fb, qw, rows, plan.cap, plan.fb_blocks, st);
+        if (s.DI == 64) return launch_prefill_hb<kBF16, 64>(hb, pa, fa, fb, qw, rows, plan.cap, plan.fb_blocks, st);
+        return launch_prefill_hb<kBF16, 128>(hb, pa, fa, fb, qw, rows, plan.cap, plan.fb_blocks, st);
+    }
+    if (s.DI == 32) return launch_prefill_hb<kF32, 32>(hb, pa, fa, fb, qw, rows, plan.cap, plan.fb_blocks, st);
+    return launch_prefill_hb<kF32, 64>(hb, pa, fa, fb, qw, rows, plan.cap, plan.fb_blocks, st);
+}
+
+template <int DT, int HB, int DI>
+static hipError_t launch_decode_t(const void* q, const float* q_scale, const void* kc, const float* k_scale,
+                                  const float* w, const int64_t* cu, int B, int HI, int max_len, float* scores,
+                                  hipStream_t st) {
+    dim3 grid((max_len + DEC_CHUNK - 1) / DEC_CHUNK, B);
+    hipLaunchKernelGGL((decode_score_kernel<DT, HB, DI>), grid, dim3(DEC_NT), 0, st,
+                       static_cast<const unsigned char*>(q), q_scale, static_cast<const unsigned char*>(kc),
+                       k_scale, w, cu, HI, scores);
+    return hipGetLastError();
+}
+
+template <int DT, int DI>
+static hipError_t launch_decode_hb(int hb, const void* q, const float* qs, const void* kc, const float* ks,
+                                   const float* w, const int64_t* cu, int B, int HI, int ml, float* sc,
+                                   hipStream_t st) {
+    if (hb == 1) return launch_decode_t<DT, 1, DI>(q, qs, kc, ks, w, cu, B, HI, ml, sc, st);
+    if (hb == 2) return launch_decode_t<DT, 2, DI>(q, qs, kc, ks, w, cu, B, HI, ml, sc, st);
+    return launch_decode_t<DT, 4, DI>(q, qs, kc, ks, w, cu, B, HI, ml, sc, st);
+}
+
+hipError_t launch_index_decode(const IndexerShape& s, const void* q, const float* q_scale, const void* kc,
+                               const float* k_scale, const float* w, const int64_t* cu, int B, int max_len,
+                               float* scores, hipStream_t st) {
+    const int hb = head_blocks(s.HI);
+    if (s.dt == kFP8) return launch_decode_hb<kFP8, 128>(hb, q, q_scale, kc, k_scale, w, cu, B, s.HI, max_len, scores, st);
+    if (s.dt == kBF16) {
+        if (s.DI == 32) return launch_decode_hb<kBF16, 32>(hb, q, q_scale, kc, k_scale, w, cu, B, s.HI, max_len, scores, st);
+        if (s.DI == 64) return launch_decode_hb<kBF16, 64>(hb, q, q_scale, kc, k_scale, w, cu, B, s.HI, max_len, scores, st);
+        return launch_decode_hb<kBF16, 128>(hb, q, q_scale, kc, k_scale, w, cu, B, s.HI, max_len, scores, st);
+    }
+    if (s.DI == 32) return launch_decode_hb<kF32, 32>(hb, q, q_scale, kc, k_scale, w, cu, B, s.HI, max_len, scores, st);
+    return launch_decode_hb<kF32, 64>(hb, q, q_scale, kc, k_scale, w, cu, B, s.HI, max_len, scores, st);
+}
+
+}  // namespace tlsl

@@ -1,0 +1,112 @@
+// topk_common.h -- workgroup-level exact top-k of one score row with the
+// lower-position tie rule (DSA page, section 1.1 eq.(2); section 2 notes radix
+// top-k with variable-length rows).
+#pragma once
+
+#include "tlsl_device.h"
+
+namespace tlsl {
+
+constexpr int TK_LCAP = 8192;  // candidate keys gathered into LDS once a bin is this small
+
+struct TopkSmem {
+    uint32_t hist[2048];
+    uint32_t lkeys[TK_LCAP];
+    int scratch[64];
+    int lcnt;
+};
+
+// Radix digits of the 32-bit score key, most significant first.
+__device__ __forceinline__ int radix_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
+__device__ __forceinline__ uint32_t radix_mask(int p) { return p == 2 ? 0x3ffu : 0x7ffu; }
+
+// Exact selection of the K = min(k, L) best of sc[0..L) ordered by (score desc,
+// position asc).  Writes S[0..k): the selected positions ascending, then -1;
+// Ss (optional): each slot's score, -inf for unused slots.  All NT threads of
+// the workgroup call it; `sc` must be visible to the whole workgroup.
+//
+// Method: three radix passes over the score key (11, 11, 10 bits) find the
+// K-th largest key T and the count gt of keys above it; once the candidate
+// bin holds at most TK_LCAP keys the remaining passes run on an LDS copy.
+// A final in-order pass keeps every key > T and the first K - gt keys == T
+// (lowest positions first).
+template <int NT>
+__device__ void block_topk_row(const float* __restrict__ sc, int L, int k, int32_t* __restrict__ S,
+                               float* __restrict__ Ss, TopkSmem& sm) {
+    const int tid = threadIdx.x;
+    const int K = min(k, L);
+    if (L <= k) {
+        for (int i = tid; i < k; i += NT) {
+            S[i] = i < L ? i : -1;
+            if (Ss) Ss[i] = i < L ? sc[i] : -INFINITY;
+        }
+        return;
+    }
+    uint32_t prefix = 0, pmask = 0;
+    int need = K, gt = 0, lcnt = 0;
+    bool in_lds = false;
+    for (int p = 0; p < 3; ++p) {
+        const int sh = radix_shift(p);
+        const uint32_t dm = radix_mask(p);
+        for (int i = tid; i < 2048; i += NT) sm.hist[i] = 0;
+        __syncthreads();
+        if (!in_lds) {
+            for (int i = tid; i < L; i += NT) {
+                uint32_t key = score_key(sc[i]);
+                if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> sh) & dm], 1u);
+            }
+        } else {
+            for (int i = tid; i < lcnt; i += NT) {
+                uint32_t key = sm.lkeys[i];
+                if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> sh) & dm], 1u);
+            }
+        }
+        __syncthreads();
+        int above;
+        const int d = block_find_bin<NT, 2048>(sm.hist, need, &above, sm.scratch);
+        const int cd = (int)sm.hist[d];
+        gt += above;
+        need -= above;
+        prefix |= (uint32_t)d << sh;
+        pmask |= dm << sh;
+        if (p < 2 && !in_lds && cd <= TK_LCAP) {
+            if (tid == 0) sm.lcnt = 0;
+            __syncthreads();
+            for (int i = tid; i < L; i += NT) {
+                uint32_t key = score_key(sc[i]);
+                if ((key & pmask) == prefix) sm.lkeys[atomicAdd(&sm.lcnt, 1)] = key;
+            }
+            __syncthreads();
+            lcnt = sm.lcnt;
+            in_lds = true;
+        }
+        __syncthreads();
+    }
+    const uint32_t T = prefix;
+    const int need_ties = K - gt;
+    int run_sel = 0, run_tie = 0;
+    for (int base = 0; base < L && run_sel < K; base += NT) {
+        const int i = base + tid;
+        const bool v = i < L;
+        const float s = v ? sc[i] : 0.f;
+        const uint32_t key = v ? score_key(s) : 0u;
+        const bool isgt = v && key > T, istie = v && key == T;
+        int rt, rdum, tt, tdum;
+        block_scan2<NT>(istie, false, &rt, &rdum, &tt, &tdum, sm.scratch);
+        const bool sel = isgt || (istie && run_tie + rt < need_ties);
+        int rs, ts;
+        block_scan2<NT>(sel, false, &rs, &rdum, &ts, &tdum, sm.scratch);
+        if (sel) {
+            S[run_sel + rs] = i;
+            if (Ss) Ss[run_sel + rs] = s;
+        }
+        run_sel += ts;
+        run_tie += tt;
+    }
+    for (int i = K + tid; i < k; i += NT) {
+        S[i] = -1;
+        if (Ss) Ss[i] = -INFINITY;
+    }
+}
+
+}  // namespace tlsl
