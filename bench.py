@@ -151,11 +151,12 @@ def bench_decode(seed, steps, warmup):
     S = torch.empty((B, k), dtype=torch.int32, device=DEV)
     out = torch.empty((B, H, Dv), dtype=torch.bfloat16, device=DEV)
     ws = torch.empty(tl.sparse_attn_decode_workspace_bytes(qa, kva, S, Dv), dtype=torch.uint8, device=DEV)
+    tws = torch.empty(tl.topk_select_workspace_bytes(B, k, max_len), dtype=torch.uint8, device=DEV)
     scale = 1.0 / math.sqrt(Dqk)
 
     def step():
         tl.index_decode(di.q, di.k, di.w, cu, max_len, q_scale=di.q_scale, k_scale=di.k_scale, scores=scores)
-        tl.topk_select(scores, row_start, row_len, k, max_len, S=S)
+        tl.topk_select(scores, row_start, row_len, k, max_len, S=S, workspace=tws)
         tl.sparse_attn_decode(qa, kva, cu, S, scale, Dv, out=out, workspace=ws)
 
     wall, ev = time_calls(step, steps, warmup)
@@ -163,7 +164,7 @@ def bench_decode(seed, steps, warmup):
     stages = {}
     for name, fn in (("index_decode", lambda: tl.index_decode(di.q, di.k, di.w, cu, max_len, q_scale=di.q_scale,
                                                                k_scale=di.k_scale, scores=scores)),
-                     ("topk_select", lambda: tl.topk_select(scores, row_start, row_len, k, max_len, S=S)),
+                     ("topk_select", lambda: tl.topk_select(scores, row_start, row_len, k, max_len, S=S, workspace=tws)),
                      ("sparse_attn_decode", lambda: tl.sparse_attn_decode(qa, kva, cu, S, scale, Dv, out=out,
                                                                           workspace=ws))):
         stages[name] = time_calls(fn, max(3, steps // 2), 1)[1]

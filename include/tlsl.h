@@ -18,13 +18,13 @@
  *    never allocates, frees or synchronises.  Layouts are dense row-major with
  *    the last dimension contiguous.  Base pointers must be 16-byte aligned.
  *  - Every call is asynchronous on `stream` (NULL = the null stream).
- *  - Scratch memory comes from the caller.  index_prefill and
+ *  - Scratch memory comes from the caller.  index_prefill, topk_select and
  *    sparse_attn_decode take a workspace: pass workspace == NULL to query its
  *    size (written to *ws_bytes, nothing is launched, TLSL_OK is returned);
  *    otherwise *ws_bytes must hold the size of `workspace`, at least the
  *    queried size.  A workspace may be reused once the call that used it has
  *    completed on its stream; calls that overlap must not share one.
- *    index_decode, topk_select and sparse_attn_prefill need no workspace:
+ *    index_decode and sparse_attn_prefill need no workspace:
  *    their workspace argument is ignored, and *ws_bytes (if ws_bytes is not
  *    NULL) receives 0.
  *  - Arguments are validated on the host before anything is launched; a
@@ -124,7 +124,8 @@ int index_decode(const void* qI, const float* q_scale, const void* kI_cache,
  *   row_start [R] int64 (device), row_len [R] int32 (device, >= 0)
  *   max_len   >= every row_len (host value)
  *   S         [R,k] int32 out, S_score [R,k] fp32 out (optional)
- * Supported: 1 <= k <= 4096, max_len < 2^31.
+ *   workspace about R*(2k+264)*8 bytes (query protocol above)
+ * Supported: 1 <= k <= 4096, 0 <= row_len < 2^31.
  */
 int topk_select(const float* scores, const int64_t* row_start, const int32_t* row_len, int R,
                 int k, int max_len, int32_t* S, float* S_score, void* workspace,

@@ -16,4 +16,5 @@ from .binding import (  # noqa: F401
     sparse_attn_decode_workspace_bytes,
     sparse_attn_prefill,
     topk_select,
+    topk_select_workspace_bytes,
 )

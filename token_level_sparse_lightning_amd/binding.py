@@ -134,8 +134,18 @@ def index_decode(qI, kI_cache, wI, cu_seqlens, max_len, q_scale=None, k_scale=No
     return scores
 
 
+def topk_select_workspace_bytes(R, k, max_len) -> int:
+    lib = load()
+    size = ctypes.c_size_t(0)
+    dummy = ctypes.c_void_p(16)
+    rc = lib.topk_select(dummy, dummy, dummy, int(R), int(k), int(max_len), dummy, None, None,
+                         ctypes.byref(size), None)
+    _check("topk_select", rc)
+    return size.value
+
+
 def topk_select(scores, row_start, row_len, k, max_len, S=None, S_score=None, want_scores=False,
-                stream=None):
+                workspace=None, stream=None):
     """Row top-k: returns (S [R,k] int32 row-relative, S_score or None)."""
     lib = load()
     R = row_len.shape[0]
@@ -143,8 +153,12 @@ def topk_select(scores, row_start, row_len, k, max_len, S=None, S_score=None, wa
         S = torch.empty((R, k), dtype=torch.int32, device=scores.device)
     if S_score is None and want_scores:
         S_score = torch.empty((R, k), dtype=torch.float32, device=scores.device)
+    if workspace is None:
+        workspace = torch.empty(topk_select_workspace_bytes(R, k, max_len), dtype=torch.uint8,
+                                device=scores.device)
+    size = ctypes.c_size_t(workspace.numel())
     rc = lib.topk_select(_ptr(scores), _ptr(row_start), _ptr(row_len), R, k, int(max_len), _ptr(S),
-                         _ptr(S_score), None, None, _stream(stream))
+                         _ptr(S_score), _ptr(workspace), ctypes.byref(size), _stream(stream))
     _check("topk_select", rc)
     return S, S_score
 

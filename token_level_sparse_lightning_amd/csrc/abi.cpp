@@ -126,7 +126,8 @@ int topk_select(const float* scores, const int64_t* row_start, const int32_t* ro
     if (!aligned16(S) || !aligned16(S_score) || !aligned16(row_start) || !aligned16(row_len))
         return fail(TLSL_ERR_ALIGN, "topk_select: pointers not 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(scores) & 3u) != 0) return fail(TLSL_ERR_ALIGN, "topk_select: scores not 4-byte aligned");
-    if (ws_bytes) *ws_bytes = 0;  // needs no workspace
+    const int rc = workspace_protocol(workspace, ws_bytes, tlsl::topk_ws_bytes(R, k, max_len));
+    if (rc) return rc > 0 ? ok() : rc;
     return launch_result(tlsl::launch_topk_select(scores, row_start, row_len, R, k, max_len, S, S_score, workspace,
                                                   stream),
                          "topk_select");

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(AttnArgs a) {
     constexpr int CROW = DQK * EB;            // bytes of one entry
     constexpr int CSTR = CROW + 16;           // padded LDS row
     constexpr int VROW = AT_TS * EB;          // bytes of one transposed value row
-    constexpr int VSTR = VROW + 16;
+    constexpr int VSTR = VROW + (EB == 2 ? 8 : 16);  // rows 8 apart land 64 words apart
     constexpr int VPC = 16 / EB;              // values per 16-B chunk
     constexpr int NDB = DV / 16;              // output dim blocks
     static_assert(DV % 16 == 0 && DV <= DQK, "value width");
@@ -110,8 +110,10 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(AttnArgs a) {
         }
         if (!__syncthreads_or(my_valid)) continue;
         // value part: item = (slot quad, chunk of VPC dims); row-major and transposed
+        // slot quad varies fastest across lanes: the transposed writes of one
+        // instruction then cover 8 rows x 8 quads, spread over all banks
         for (int it = tid; it < (AT_TS / 4) * (DV / VPC); it += NT) {
-            const int qd = it / (DV / VPC), oc = it % (DV / VPC);
+            const int qd = it % (AT_TS / 4), oc = it / (AT_TS / 4);
             uint4 v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -253,33 +255,46 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(AttnArgs a) {
 }
 
 // Merge the split partials of a decode row: o = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s.
+// One workgroup per (row, head); each thread owns DV/CB_NT consecutive dims.
+constexpr int CB_NT = 128;
+
 template <int DT, int DV>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* part_o, const float* part_ml, int H, int nsplit,
-                                                           unsigned char* out, float* lse) {
+__global__ __launch_bounds__(CB_NT) void attn_combine_kernel(const float* part_o, const float* part_ml, int H, int nsplit,
+                                                             unsigned char* out, float* lse) {
     constexpr int EB = ElemBytes<DT>::v;
-    const int row = blockIdx.x;
-    for (int idx = threadIdx.x; idx < H * DV; idx += 256) {
-        const int h = idx / DV, d = idx % DV;
-        float M = -INFINITY;
-        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(((size_t)row * nsplit + s) * H + h) * 2]);
-        float L = 0.f, acc = 0.f;
-        if (M != -INFINITY) {
-            for (int s = 0; s < nsplit; ++s) {
-                const size_t pidx = ((size_t)row * nsplit + s) * H + h;
-                const float ms = part_ml[pidx * 2];
-                const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
-                L += f * part_ml[pidx * 2 + 1];
-                acc += f * part_o[pidx * DV + d];
+    constexpr int PER = (DV + CB_NT - 1) / CB_NT;
+    const int row = blockIdx.x / H, h = blockIdx.x % H;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(((size_t)row * nsplit + s) * H + h) * 2]);
+    float L = 0.f, acc[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < nsplit; ++s) {
+            const size_t pidx = ((size_t)row * nsplit + s) * H + h;
+            const float ms = part_ml[pidx * 2];
+            const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
+            L += f * part_ml[pidx * 2 + 1];
+            const float* po = part_o + pidx * DV;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                const int d = threadIdx.x * PER + j;
+                if (d < DV) acc[j] += f * po[d];
             }
         }
-        const float v = L > 0.f ? acc / L : 0.f;
-        const size_t oi = ((size_t)row * H + h) * DV + d;
-        if constexpr (EB == 2)
-            reinterpret_cast<uint16_t*>(out)[oi] = f32_to_bf16_rne(v);
-        else
-            reinterpret_cast<float*>(out)[oi] = v;
-        if (lse && d == 0) lse[(size_t)row * H + h] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
     }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const size_t ob = ((size_t)row * H + h) * DV;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int d = threadIdx.x * PER + j;
+        if (d >= DV) continue;
+        if constexpr (EB == 2)
+            reinterpret_cast<uint16_t*>(out)[ob + d] = f32_to_bf16_rne(acc[j] * inv);
+        else
+            reinterpret_cast<float*>(out)[ob + d] = acc[j] * inv;
+    }
+    if (lse && threadIdx.x == 0) lse[(size_t)row * H + h] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -360,11 +375,11 @@ hipError_t launch_sparse_attn_decode(const AttnShape& s, const void* q, const vo
     dispatch_attn<true>(s, a, B * ns, st);
     if (ns > 1) {
         if (s.dt == kBF16)
-            hipLaunchKernelGGL((attn_combine_kernel<kBF16, 512>), dim3(B), dim3(256), 0, st, a.part_o, a.part_ml, s.H, ns,
-                               a.out, lse);
+            hipLaunchKernelGGL((attn_combine_kernel<kBF16, 512>), dim3(B * s.H), dim3(CB_NT), 0, st, a.part_o, a.part_ml,
+                               s.H, ns, a.out, lse);
         else
-            hipLaunchKernelGGL((attn_combine_kernel<kF32, 64>), dim3(B), dim3(256), 0, st, a.part_o, a.part_ml, s.H, ns,
-                               a.out, lse);
+            hipLaunchKernelGGL((attn_combine_kernel<kF32, 64>), dim3(B * s.H), dim3(CB_NT), 0, st, a.part_o, a.part_ml,
+                               s.H, ns, a.out, lse);
     }
     return hipGetLastError();
 }

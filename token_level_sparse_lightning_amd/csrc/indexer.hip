@@ -489,7 +489,7 @@ __global__ __launch_bounds__(FB_NT) void prefill_fallback_kernel(FallbackArgs a)
 // Decode scan: one query per sequence against its packed key cache.
 // ---------------------------------------------------------------------------
 constexpr int DEC_NT = 256;
-constexpr int DEC_CHUNK = 2048;  // keys per workgroup
+constexpr int DEC_CHUNK = 4096;  // keys per workgroup
 
 template <int DT, int HB, int DI>
 __global__ __launch_bounds__(DEC_NT) void decode_score_kernel(const unsigned char* q, const float* q_scale,
@@ -510,13 +510,28 @@ __global__ __launch_bounds__(DEC_NT) void decode_score_kernel(const unsigned cha
     I::load_query(q + (size_t)b * HI * I::ROWB, w + (size_t)b * HI, wmul, HI, true, qf, wv);
     const unsigned char* kb_base = kc + (size_t)start * I::ROWB;
     const int end = min(L, base + DEC_CHUNK);
-    for (int j0 = base + 64 * wv_id; j0 < end; j0 += 64 * (DEC_NT / 64)) {
-        uint4 kf[4][NCH];
-        I::load_keys_global(kb_base, j0, L - 1, kf);
-        float s = I::score(qf, wv, kf);
-        const int key = j0 + l;
-        if (DT == kFP8) s *= k_scale[start + min(key, L - 1)];
-        if (key < L) scores[start + key] = s;
+    constexpr int STEP = 64 * (DEC_NT / 64);
+    // two subtiles in flight per wave: the next one loads while this one is scored
+    uint4 kf[2][4][NCH];
+    int j0 = base + 64 * wv_id;
+    if (j0 < end) I::load_keys_global(kb_base, j0, L - 1, kf[0]);
+    for (; j0 < end; j0 += 2 * STEP) {
+        const int j1 = j0 + STEP;
+        if (j1 < end) I::load_keys_global(kb_base, j1, L - 1, kf[1]);
+        {
+            float s = I::score(qf, wv, kf[0]);
+            const int key = j0 + l;
+            if (DT == kFP8) s *= k_scale[start + min(key, L - 1)];
+            if (key < L) scores[start + key] = s;
+        }
+        if (j1 >= end) break;
+        if (j1 + STEP < end) I::load_keys_global(kb_base, j1 + STEP, L - 1, kf[0]);
+        {
+            float s = I::score(qf, wv, kf[1]);
+            const int key = j1 + l;
+            if (DT == kFP8) s *= k_scale[start + min(key, L - 1)];
+            if (key < L) scores[start + key] = s;
+        }
     }
 }
 

@@ -1,29 +1,261 @@
 // topk.hip -- topk_select: exact top-k of explicit variable-length score rows
 // (DSA page, section 1.1 eq.(2); section 2 on radix top-k over rows given by
-// sequence lengths).  One workgroup per row runs the radix select of
-// topk_common.h.
+// sequence lengths, avoiding a full sort).
+//
+// Three launches, every one spread over many workgroups:
+//  1. topk_threshold: per row, the r-th largest of a strided sample of the
+//     row (r = expected sample hits inside the top-k plus 4 standard
+//     deviations) -- a conservative threshold.
+//  2. topk_filter: workgroups over (row chunk) append every (score, position)
+//     at or above the row's threshold to the row's candidate buffer.
+//  3. topk_final: per row, an exact radix select among the candidates in LDS,
+//     ties resolved to the lowest positions, and the selected positions
+//     written in ascending order through a position bitmap.  A row whose
+//     candidates miss (the sample threshold overshot) or overflow is selected
+//     from its full score row instead (topk_common.h).
+// The result never depends on the threshold, only the work does.
+#include <math.h>
+
 #include "tlsl_device.h"
 #include "tlsl_internal.h"
 #include "topk_common.h"
 
 namespace tlsl {
 
-constexpr int TS_NT = 512;
+constexpr int TT_NT = 256;              // threshold workgroup
+constexpr int TT_SAMPLE_MAX = 8192;     // sample values held in LDS
+constexpr int TF_NT = 256;              // filter workgroup
+constexpr int TF_PER = 16;              // scores per filter thread
+constexpr int TF_CHUNK = TF_NT * TF_PER;
+constexpr int TFIN_NT = 512;            // final workgroup
+constexpr int TSEL_CAPMAX = 8448;       // candidate buffer entries per row, max
+constexpr int TSEL_BITMAP_WORDS = 4096; // rows up to 131072 use the bitmap output
+constexpr float TSEL_SIGMA = 4.0f;
 
-__global__ __launch_bounds__(TS_NT) void topk_select_kernel(const float* scores, const int64_t* row_start,
-                                                            const int32_t* row_len, int k, int32_t* S,
-                                                            float* Ss) {
-    __shared__ TopkSmem sm;
-    const int r = blockIdx.x;
-    const int L = max(row_len[r], 0);
-    block_topk_row<TS_NT>(scores + row_start[r], L, k, S + (size_t)r * k, Ss ? Ss + (size_t)r * k : nullptr, sm);
+struct TopkArgs {
+    const float* scores;
+    const int64_t* row_start;
+    const int32_t* row_len;
+    int k, cap;
+    float* theta;   // [R]
+    int* cnt;       // [R]
+    uint2* buf;     // [R][cap]
+    int32_t* S;
+    float* Ss;
+};
+
+// Exclusive scan of an int over the workgroup; scratch >= NT/64 + 1 ints.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* total, int* scratch) {
+    constexpr int NW = NT / 64;
+    const int w = threadIdx.x >> 6, l = lane_id();
+    const int incl = wave_incl_scan(v);
+    if (l == 63) scratch[w] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int c = scratch[i];
+        if (i < w) base += c;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + incl - v;
 }
 
-size_t topk_ws_bytes(int, int, int) { return 0; }
+// need-th largest (1-based) of key(i) over i < cnt with valid(i), keys in LDS
+// or registers; three radix passes (11, 11, 10 bits).  *gt = count of valid
+// keys strictly above the result.
+template <int NT, class KeyFn>
+__device__ uint32_t block_select_lds(int cnt, int need, KeyFn key_of, uint32_t* hist, int* scratch, int* gt_out) {
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0, pmask = 0;
+    int gt = 0;
+    for (int p = 0; p < 3; ++p) {
+        const int sh = radix_shift(p);
+        const uint32_t dm = radix_mask(p);
+        for (int i = tid; i < 2048; i += NT) hist[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < cnt; i += NT) {
+            bool ok;
+            const uint32_t key = key_of(i, &ok);
+            if (ok && (key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
+        }
+        __syncthreads();
+        int above;
+        const int d = block_find_bin<NT, 2048>(hist, need, &above, scratch);
+        gt += above;
+        need -= above;
+        prefix |= (uint32_t)d << sh;
+        pmask |= dm << sh;
+    }
+    *gt_out = gt;
+    return prefix;
+}
 
-hipError_t launch_topk_select(const float* scores, const int64_t* row_start, const int32_t* row_len, int R,
-                              int k, int, int32_t* S, float* S_score, void*, hipStream_t st) {
-    hipLaunchKernelGGL(topk_select_kernel, dim3(R), dim3(TS_NT), 0, st, scores, row_start, row_len, k, S, S_score);
+__device__ __forceinline__ int sample_stride(int L) { return max(16, (L + TT_SAMPLE_MAX - 1) / TT_SAMPLE_MAX); }
+
+__global__ __launch_bounds__(TT_NT) void topk_threshold_kernel(TopkArgs a) {
+    __shared__ uint32_t skeys[TT_SAMPLE_MAX];
+    __shared__ uint32_t hist[2048];
+    __shared__ int scratch[64];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int L = max(a.row_len[r], 0);
+    if (tid == 0) a.cnt[r] = 0;
+    const int K = min(a.k, L);
+    const int stride = sample_stride(L);
+    const int ns = L > 0 ? (L - 1) / stride + 1 : 0;
+    const float mu = L > 0 ? (float)ns * (float)K / (float)L : 0.f;
+    const int need = (int)ceilf(mu + TSEL_SIGMA * sqrtf(mu)) + 2;
+    if (L <= a.cap || need >= ns) {
+        if (tid == 0) a.theta[r] = -INFINITY;
+        return;
+    }
+    const float* sc = a.scores + a.row_start[r];
+    for (int j = tid; j < ns; j += TT_NT) skeys[j] = score_key(sc[(size_t)j * stride]);
+    __syncthreads();
+    int gt;
+    const uint32_t T = block_select_lds<TT_NT>(ns, need, [&](int i, bool* ok) { *ok = true; return skeys[i]; }, hist,
+                                               scratch, &gt);
+    if (tid == 0) a.theta[r] = key_score(T);
+}
+
+__global__ __launch_bounds__(TF_NT) void topk_filter_kernel(TopkArgs a) {
+    const int r = blockIdx.y;
+    const int L = max(a.row_len[r], 0);
+    const int base = blockIdx.x * TF_CHUNK;
+    if (base >= L) return;
+    const float th = a.theta[r];
+    const float* sc = a.scores + a.row_start[r];
+    uint2* out = a.buf + (size_t)r * a.cap;
+    const int l = lane_id();
+    float v[TF_PER];
+#pragma unroll
+    for (int i = 0; i < TF_PER; ++i) {
+        const int idx = base + i * TF_NT + threadIdx.x;
+        v[i] = idx < L ? sc[idx] : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < TF_PER; ++i) {
+        const int idx = base + i * TF_NT + threadIdx.x;
+        const bool ok = idx < L && v[i] >= th;
+        const uint64_t m = ballot(ok);
+        if (m) {
+            int slot = 0;
+            if (l == (int)__builtin_ctzll(m)) slot = atomicAdd(&a.cnt[r], __popcll(m));
+            slot = __shfl(slot, (int)__builtin_ctzll(m), 64) + rank_below(m);
+            if (ok && slot < a.cap) out[slot] = make_uint2(__float_as_uint(v[i]), (uint32_t)idx);
+        }
+    }
+}
+
+struct TopkFinalSmem {
+    uint32_t keys[TSEL_CAPMAX];
+    uint32_t pos[TSEL_CAPMAX];
+    uint32_t bitmap[TSEL_BITMAP_WORDS];
+    uint32_t hist[2048];
+    int scratch[64];
+};
+
+union TopkFinalShared {
+    TopkFinalSmem f;
+    TopkSmem g;
+};
+
+__global__ __launch_bounds__(TFIN_NT) void topk_final_kernel(TopkArgs a) {
+    __shared__ TopkFinalShared sh;
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int L = max(a.row_len[r], 0);
+    const int K = min(a.k, L);
+    const float* sc = a.scores + a.row_start[r];
+    int32_t* Srow = a.S + (size_t)r * a.k;
+    float* Ssrow = a.Ss ? a.Ss + (size_t)r * a.k : nullptr;
+    const int cnt = a.cnt[r];
+    const int nwords = (L + 31) / 32;
+    if (L > a.k && (cnt < K || cnt > a.cap || nwords > TSEL_BITMAP_WORDS)) {
+        block_topk_row<TFIN_NT>(sc, L, a.k, Srow, Ssrow, sh.g);
+        return;
+    }
+    if (L <= a.k) {
+        for (int i = tid; i < a.k; i += TFIN_NT) {
+            Srow[i] = i < L ? i : -1;
+            if (Ssrow) Ssrow[i] = i < L ? sc[i] : -INFINITY;
+        }
+        return;
+    }
+    TopkFinalSmem& s = sh.f;
+    const uint2* src = a.buf + (size_t)r * a.cap;
+    for (int i = tid; i < cnt; i += TFIN_NT) {
+        const uint2 e = src[i];
+        s.keys[i] = score_key(__uint_as_float(e.x));
+        s.pos[i] = e.y;
+    }
+    for (int i = tid; i < nwords; i += TFIN_NT) s.bitmap[i] = 0u;
+    __syncthreads();
+    int gt;
+    const uint32_t T = block_select_lds<TFIN_NT>(cnt, K, [&](int i, bool* ok) { *ok = true; return s.keys[i]; }, s.hist,
+                                                 s.scratch, &gt);
+    // ties at T: keep the (K - gt) lowest positions -> largest inverted position
+    const int need_ties = K - gt;
+    int tgt;
+    const uint32_t inv_cut = block_select_lds<TFIN_NT>(
+        cnt, need_ties, [&](int i, bool* ok) { *ok = s.keys[i] == T; return ~s.pos[i]; }, s.hist, s.scratch, &tgt);
+    for (int i = tid; i < cnt; i += TFIN_NT) {
+        const uint32_t key = s.keys[i];
+        if (key > T || (key == T && ~s.pos[i] >= inv_cut)) atomicOr(&s.bitmap[s.pos[i] >> 5], 1u << (s.pos[i] & 31));
+    }
+    __syncthreads();
+    // ordered output: each thread owns a contiguous run of bitmap words
+    const int per = (nwords + TFIN_NT - 1) / TFIN_NT;
+    const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
+    int mine = 0;
+    for (int wd = w0; wd < w1; ++wd) mine += __popc(s.bitmap[wd]);
+    int total;
+    int o = block_excl_scan<TFIN_NT>(mine, &total, s.scratch);
+    for (int wd = w0; wd < w1; ++wd) {
+        uint32_t bits = s.bitmap[wd];
+        while (bits) {
+            const int b = __builtin_ctz(bits);
+            bits &= bits - 1;
+            const int p = wd * 32 + b;
+            Srow[o] = p;
+            if (Ssrow) Ssrow[o] = sc[p];
+            ++o;
+        }
+    }
+    for (int i = K + tid; i < a.k; i += TFIN_NT) {
+        Srow[i] = -1;
+        if (Ssrow) Ssrow[i] = -INFINITY;
+    }
+}
+
+static int topk_cap(int k) { return (int)((2 * (size_t)k + 256 + 255) / 256 * 256); }
+
+static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t topk_ws_bytes(int R, int k, int) {
+    return a256((size_t)R * sizeof(float)) + a256((size_t)R * sizeof(int)) + a256((size_t)R * topk_cap(k) * sizeof(uint2));
+}
+
+hipError_t launch_topk_select(const float* scores, const int64_t* row_start, const int32_t* row_len, int R, int k,
+                              int max_len, int32_t* S, float* S_score, void* ws, hipStream_t st) {
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    TopkArgs a;
+    a.scores = scores;
+    a.row_start = row_start;
+    a.row_len = row_len;
+    a.k = k;
+    a.cap = topk_cap(k);
+    a.theta = reinterpret_cast<float*>(w);
+    a.cnt = reinterpret_cast<int*>(w + a256((size_t)R * sizeof(float)));
+    a.buf = reinterpret_cast<uint2*>(w + a256((size_t)R * sizeof(float)) + a256((size_t)R * sizeof(int)));
+    a.S = S;
+    a.Ss = S_score;
+    hipLaunchKernelGGL(topk_threshold_kernel, dim3(R), dim3(TT_NT), 0, st, a);
+    const int chunks = max_len > 0 ? (max_len + TF_CHUNK - 1) / TF_CHUNK : 1;
+    hipLaunchKernelGGL(topk_filter_kernel, dim3(chunks, R), dim3(TF_NT), 0, st, a);
+    hipLaunchKernelGGL(topk_final_kernel, dim3(R), dim3(TFIN_NT), 0, st, a);
     return hipGetLastError();
 }
 
