@@ -222,6 +222,8 @@ def main():
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--long", action="store_true", help="also time the n=131072 prefill")
     ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--only", default="", help="comma list of extra workloads to run: "
+                    "prefill_fp8,attn_prefill,decode,prefill_long (default: all but prefill_long)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -233,15 +235,21 @@ def main():
 
     head, inp, S = bench_prefill(8192, synth.DT_BF16, args.seed, args.steps, args.warmup)
     extra = {}
+    want = set(args.only.split(",")) if args.only else {"prefill_fp8", "attn_prefill", "decode"}
+    if args.long:
+        want.add("prefill_long")
     if not args.quick:
-        fp8, _, S3 = bench_prefill(32768, synth.DT_FP8, args.seed + 1, max(5, args.steps // 2), 2)
-        extra["prefill_fp8"] = fp8
-        extra["attn_prefill"] = bench_attn_prefill(S3, 32768, args.seed + 1, max(3, args.steps // 4), 1)
-        del S3
-        torch.cuda.empty_cache()
-        extra["decode"] = bench_decode(args.seed + 3, args.steps, args.warmup)
-        torch.cuda.empty_cache()
-        if args.long:
+        if want & {"prefill_fp8", "attn_prefill"}:
+            fp8, _, S3 = bench_prefill(32768, synth.DT_FP8, args.seed + 1, max(5, args.steps // 2), 2)
+            extra["prefill_fp8"] = fp8
+            if "attn_prefill" in want:
+                extra["attn_prefill"] = bench_attn_prefill(S3, 32768, args.seed + 1, max(3, args.steps // 4), 1)
+            del S3
+            torch.cuda.empty_cache()
+        if "decode" in want:
+            extra["decode"] = bench_decode(args.seed + 3, args.steps, args.warmup)
+            torch.cuda.empty_cache()
+        if "prefill_long" in want:
             lg, _, _ = bench_prefill(131072, synth.DT_FP8, args.seed + 4, 3, 1, plant_max_dist=100000)
             extra["prefill_long"] = lg
     cpu = None if args.no_cpu else cpu_baseline(inp, 2048, 8192)

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(AttnArgs a) {
     constexpr int CROW = DQK * EB;            // bytes of one entry
     constexpr int CSTR = CROW + 16;           // padded LDS row
     constexpr int VROW = AT_TS * EB;          // bytes of one transposed value row
-    constexpr int VSTR = VROW + (EB == 2 ? 8 : 16);  // rows 8 apart land 64 words apart
+    constexpr int VSTR = VROW + 16;  // 16-byte aligned rows for the 16-byte fragment reads
     constexpr int VPC = 16 / EB;              // values per 16-B chunk
     constexpr int NDB = DV / 16;              // output dim blocks
     static_assert(DV % 16 == 0 && DV <= DQK, "value width");

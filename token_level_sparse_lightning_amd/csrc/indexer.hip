@@ -27,6 +27,8 @@
 // prefill row at the same length bit for bit.
 #include <math.h>
 
+#include <algorithm>
+
 #include "tlsl_device.h"
 #include "tlsl_internal.h"
 #include "topk_common.h"
@@ -535,9 +537,123 @@ __global__ __launch_bounds__(DEC_NT) void decode_score_kernel(const unsigned cha
     }
 }
 
+// Balanced decode scan: the batch is cut into sequence-aligned 64-key
+// subtiles; workgroup i takes an equal contiguous range of them (the subtile
+// prefix over the sequences is rebuilt in LDS by every workgroup), its waves
+// interleave over the range, and each wave keeps the next subtile's keys in
+// flight while it scores the current one.  Every workgroup has the same amount
+// of work and no workgroup is launched for keys past a sequence's end.
+constexpr int DEC2_NT = 256;
+constexpr int DEC2_MAXB = 4096;
+
+__device__ __forceinline__ int find_seq(const int* pre, int B, int g) {
+    int lo = 0, hi = B;  // pre[lo] <= g < pre[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] <= g) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+template <int DT, int HB, int DI>
+__global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned char* q, const float* q_scale,
+                                                              const unsigned char* kc, const float* k_scale,
+                                                              const float* w, const int64_t* cu, int B, int HI,
+                                                              float* scores) {
+    using I = Idx<DT, HB, DI>;
+    constexpr int NCH = I::NCH;
+    constexpr int NWV = DEC2_NT / 64;
+    __shared__ int pre[DEC2_MAXB + 1];
+    __shared__ int scratch[16];
+    const int tid = threadIdx.x, wv_id = tid >> 6, l = lane_id();
+    // subtile prefix over the sequences
+    int carry = 0;
+    for (int b0 = 0; b0 < B; b0 += DEC2_NT) {
+        const int b = b0 + tid;
+        const int ns = b < B ? (int)((cu[b + 1] - cu[b] + 63) >> 6) : 0;
+        int incl = wave_incl_scan(ns);
+        if (l == 63) scratch[wv_id] = incl;
+        __syncthreads();
+        int wbase = carry, tot = 0;
+        for (int i = 0; i < NWV; ++i) {
+            if (i < wv_id) wbase += scratch[i];
+            tot += scratch[i];
+        }
+        if (b < B) pre[b] = wbase + incl - ns;
+        carry += tot;
+        __syncthreads();
+    }
+    if (tid == 0) pre[B] = carry;
+    __syncthreads();
+    const int total = carry;
+    const int per = (total + gridDim.x - 1) / gridDim.x;
+    const int g0 = blockIdx.x * per, g1 = min(total, g0 + per);
+
+    int cur_b = -1;
+    uint4 qf[HB][NCH];
+    float wv[HB][4];
+    uint4 kf[2][4][NCH];
+    auto locate = [&](int g, int& b, int& key0, int& L, int64_t& start) {
+        b = find_seq(pre, B, g);
+        start = cu[b];
+        L = (int)(cu[b + 1] - start);
+        key0 = (g - pre[b]) * 64;
+    };
+    int g = g0 + wv_id;
+    int b, key0, L;
+    int64_t start;
+    if (g < g1) {
+        locate(g, b, key0, L, start);
+        I::load_keys_global(kc + (size_t)start * I::ROWB, key0, L - 1, kf[0]);
+    }
+    auto finish = [&](int bb, int k0, int LL, int64_t st, const uint4 (&kk)[4][NCH]) {
+        if (bb != cur_b) {
+            const float wmul = (DT == kFP8) ? q_scale[bb] : 1.f;
+            I::load_query(q + (size_t)bb * HI * I::ROWB, w + (size_t)bb * HI, wmul, HI, true, qf, wv);
+            cur_b = bb;
+        }
+        float s = I::score(qf, wv, kk);
+        const int key = k0 + l;
+        if (DT == kFP8) s *= k_scale[st + min(key, LL - 1)];
+        if (key < LL) scores[st + key] = s;
+    };
+    // two register buffers, alternated by explicit unrolling (no dynamic indexing)
+    for (; g < g1; g += 2 * NWV) {
+        int b1 = 0, k1 = 0, L1 = 0;
+        int64_t s1 = 0;
+        const int ga = g + NWV;
+        if (ga < g1) {
+            locate(ga, b1, k1, L1, s1);
+            I::load_keys_global(kc + (size_t)s1 * I::ROWB, k1, L1 - 1, kf[1]);
+        }
+        finish(b, key0, L, start, kf[0]);
+        if (ga >= g1) break;
+        const int gb = ga + NWV;
+        if (gb < g1) {
+            locate(gb, b, key0, L, start);
+            I::load_keys_global(kc + (size_t)start * I::ROWB, key0, L - 1, kf[0]);
+        }
+        finish(b1, k1, L1, s1, kf[1]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
+// Compute units of the current device (queried once per device).
+static int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 bool indexer_supported(const IndexerShape& s) {
     if (s.HI < 1 || s.HI > 64) return false;
     if (s.dt == kFP8) return s.DI == 128;
@@ -663,6 +779,23 @@ template <int DT, int HB, int DI>
 static hipError_t launch_decode_t(const void* q, const float* q_scale, const void* kc, const float* k_scale,
                                   const float* w, const int64_t* cu, int B, int HI, int max_len, float* scores,
                                   hipStream_t st) {
+    if (B <= DEC2_MAXB) {
+        // enough resident workgroups to fill every CU a few times over; each
+        // gets an equal share of the batch's subtiles
+        static int per_cu = 0;  // resident workgroups per CU for this instantiation
+        if (per_cu == 0) {
+            int nb = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_scan_kernel<DT, HB, DI>, DEC2_NT, 0) != hipSuccess ||
+                nb <= 0)
+                nb = 2;
+            per_cu = nb;
+        }
+        const int grid = std::min(device_cu_count() * per_cu, std::max(1, (int)(((int64_t)max_len * B + 63) / 64)));
+        hipLaunchKernelGGL((decode_scan_kernel<DT, HB, DI>), dim3(grid), dim3(DEC2_NT), 0, st,
+                           static_cast<const unsigned char*>(q), q_scale, static_cast<const unsigned char*>(kc),
+                           k_scale, w, cu, B, HI, scores);
+        return hipGetLastError();
+    }
     dim3 grid((max_len + DEC_CHUNK - 1) / DEC_CHUNK, B);
     hipLaunchKernelGGL((decode_score_kernel<DT, HB, DI>), grid, dim3(DEC_NT), 0, st,
                        static_cast<const unsigned char*>(q), q_scale, static_cast<const unsigned char*>(kc),

@@ -30,6 +30,7 @@ constexpr int TF_CHUNK = TF_NT * TF_PER;
 constexpr int TFIN_NT = 512;            // final workgroup
 constexpr int TSEL_CAPMAX = 8448;       // candidate buffer entries per row, max
 constexpr int TSEL_BITMAP_WORDS = 4096; // rows up to 131072 use the bitmap output
+constexpr int TSEL_CNT_STRIDE = 32;   // one 128-byte line per row counter
 constexpr float TSEL_SIGMA = 4.0f;
 
 struct TopkArgs {
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(TT_NT) void topk_threshold_kernel(TopkArgs a) {
     __shared__ int scratch[64];
     const int r = blockIdx.x, tid = threadIdx.x;
     const int L = max(a.row_len[r], 0);
-    if (tid == 0) a.cnt[r] = 0;
+    if (tid == 0) a.cnt[r * TSEL_CNT_STRIDE] = 0;
     const int K = min(a.k, L);
     const int stride = sample_stride(L);
     const int ns = L > 0 ? (L - 1) / stride + 1 : 0;
@@ -126,27 +127,43 @@ __global__ __launch_bounds__(TF_NT) void topk_filter_kernel(TopkArgs a) {
     const int L = max(a.row_len[r], 0);
     const int base = blockIdx.x * TF_CHUNK;
     if (base >= L) return;
+    __shared__ int wsum[TF_NT / 64 + 1];
     const float th = a.theta[r];
     const float* sc = a.scores + a.row_start[r];
     uint2* out = a.buf + (size_t)r * a.cap;
-    const int l = lane_id();
+    const int w = threadIdx.x >> 6;
     float v[TF_PER];
 #pragma unroll
     for (int i = 0; i < TF_PER; ++i) {
         const int idx = base + i * TF_NT + threadIdx.x;
         v[i] = idx < L ? sc[idx] : -INFINITY;
     }
+    // count first, then reserve the workgroup's slots with a single atomic
+    uint64_t m[TF_PER];
+    int mine = 0;
 #pragma unroll
     for (int i = 0; i < TF_PER; ++i) {
         const int idx = base + i * TF_NT + threadIdx.x;
-        const bool ok = idx < L && v[i] >= th;
-        const uint64_t m = ballot(ok);
-        if (m) {
-            int slot = 0;
-            if (l == (int)__builtin_ctzll(m)) slot = atomicAdd(&a.cnt[r], __popcll(m));
-            slot = __shfl(slot, (int)__builtin_ctzll(m), 64) + rank_below(m);
-            if (ok && slot < a.cap) out[slot] = make_uint2(__float_as_uint(v[i]), (uint32_t)idx);
-        }
+        m[i] = ballot(idx < L && v[i] >= th);
+        mine += __popcll(m[i]);
+    }
+    if (lane_id() == 0) wsum[w] = mine;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int tot = 0;
+        for (int i = 0; i < TF_NT / 64; ++i) tot += wsum[i];
+        wsum[TF_NT / 64] = tot > 0 ? atomicAdd(&a.cnt[r * TSEL_CNT_STRIDE], tot) : 0;
+    }
+    __syncthreads();
+    int slot = wsum[TF_NT / 64];
+    for (int i = 0; i < w; ++i) slot += wsum[i];
+#pragma unroll
+    for (int i = 0; i < TF_PER; ++i) {
+        const int idx = base + i * TF_NT + threadIdx.x;
+        const bool ok = (m[i] >> lane_id()) & 1ull;
+        const int s = slot + rank_below(m[i]);
+        if (ok && s < a.cap) out[s] = make_uint2(__float_as_uint(v[i]), (uint32_t)idx);
+        slot += __popcll(m[i]);
     }
 }
 
@@ -171,7 +188,7 @@ __global__ __launch_bounds__(TFIN_NT) void topk_final_kernel(TopkArgs a) {
     const float* sc = a.scores + a.row_start[r];
     int32_t* Srow = a.S + (size_t)r * a.k;
     float* Ssrow = a.Ss ? a.Ss + (size_t)r * a.k : nullptr;
-    const int cnt = a.cnt[r];
+    const int cnt = a.cnt[r * TSEL_CNT_STRIDE];
     const int nwords = (L + 31) / 32;
     if (L > a.k && (cnt < K || cnt > a.cap || nwords > TSEL_BITMAP_WORDS)) {
         block_topk_row<TFIN_NT>(sc, L, a.k, Srow, Ssrow, sh.g);
@@ -235,7 +252,7 @@ static int topk_cap(int k) { return (int)((2 * (size_t)k + 256 + 255) / 256 * 25
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t topk_ws_bytes(int R, int k, int) {
-    return a256((size_t)R * sizeof(float)) + a256((size_t)R * sizeof(int)) + a256((size_t)R * topk_cap(k) * sizeof(uint2));
+    return a256((size_t)R * sizeof(float)) + a256((size_t)R * TSEL_CNT_STRIDE * sizeof(int)) + a256((size_t)R * topk_cap(k) * sizeof(uint2));
 }
 
 hipError_t launch_topk_select(const float* scores, const int64_t* row_start, const int32_t* row_len, int R, int k,
@@ -249,7 +266,7 @@ hipError_t launch_topk_select(const float* scores, const int64_t* row_start, con
     a.cap = topk_cap(k);
     a.theta = reinterpret_cast<float*>(w);
     a.cnt = reinterpret_cast<int*>(w + a256((size_t)R * sizeof(float)));
-    a.buf = reinterpret_cast<uint2*>(w + a256((size_t)R * sizeof(float)) + a256((size_t)R * sizeof(int)));
+    a.buf = reinterpret_cast<uint2*>(w + a256((size_t)R * sizeof(float)) + a256((size_t)R * TSEL_CNT_STRIDE * sizeof(int)));
     a.S = S;
     a.Ss = S_score;
     hipLaunchKernelGGL(topk_threshold_kernel, dim3(R), dim3(TT_NT), 0, st, a);
