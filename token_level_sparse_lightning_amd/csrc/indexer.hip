@@ -80,7 +80,7 @@ struct Idx {
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) p = __builtin_fmaf(wv[hb][r], fmaxf(acc[hb][r], 0.f), p);
+                for (int r = 0; r < 4; ++r) p = __builtin_fmaf(wv[hb][r], relu(acc[hb][r]), p);
             part[kb] = p;
         }
         return reduce_heads_64(part);
@@ -565,12 +565,14 @@ __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned cha
     constexpr int NCH = I::NCH;
     constexpr int NWV = DEC2_NT / 64;
     __shared__ int pre[DEC2_MAXB + 1];
+    __shared__ int64_t sstart[DEC2_MAXB + 1];
     __shared__ int scratch[16];
     const int tid = threadIdx.x, wv_id = tid >> 6, l = lane_id();
-    // subtile prefix over the sequences
+    // subtile prefix over the sequences, and the sequence starts
     int carry = 0;
     for (int b0 = 0; b0 < B; b0 += DEC2_NT) {
         const int b = b0 + tid;
+        if (b <= B) sstart[b] = cu[b];
         const int ns = b < B ? (int)((cu[b + 1] - cu[b] + 63) >> 6) : 0;
         int incl = wave_incl_scan(ns);
         if (l == 63) scratch[wv_id] = incl;
@@ -590,51 +592,52 @@ __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned cha
     const int per = (total + gridDim.x - 1) / gridDim.x;
     const int g0 = blockIdx.x * per, g1 = min(total, g0 + per);
 
-    int cur_b = -1;
     uint4 qf[HB][NCH];
     float wv[HB][4];
     uint4 kf[2][4][NCH];
-    auto locate = [&](int g, int& b, int& key0, int& L, int64_t& start) {
-        b = find_seq(pre, B, g);
-        start = cu[b];
-        L = (int)(cu[b + 1] - start);
-        key0 = (g - pre[b]) * 64;
-    };
+    // the wave's subtiles are g0+wv_id, +NWV, ...; they are walked one sequence
+    // (segment) at a time so that the inner loop has straight-line loads
     int g = g0 + wv_id;
-    int b, key0, L;
-    int64_t start;
-    if (g < g1) {
-        locate(g, b, key0, L, start);
-        I::load_keys_global(kc + (size_t)start * I::ROWB, key0, L - 1, kf[0]);
-    }
-    auto finish = [&](int bb, int k0, int LL, int64_t st, const uint4 (&kk)[4][NCH]) {
-        if (bb != cur_b) {
-            const float wmul = (DT == kFP8) ? q_scale[bb] : 1.f;
-            I::load_query(q + (size_t)bb * HI * I::ROWB, w + (size_t)bb * HI, wmul, HI, true, qf, wv);
-            cur_b = bb;
+    while (g < g1) {
+        const int b = find_seq(pre, B, g);
+        const int seg_end = min(g1, pre[b + 1]);
+        const int64_t start = sstart[b];
+        const int L = (int)(sstart[b + 1] - start);
+        const unsigned char* kbase = kc + (size_t)start * I::ROWB;
+        const float wmul = (DT == kFP8) ? q_scale[b] : 1.f;
+        I::load_query(q + (size_t)b * HI * I::ROWB, w + (size_t)b * HI, wmul, HI, true, qf, wv);
+        int key0 = (g - pre[b]) * 64;
+        I::load_keys_global(kbase, key0, L - 1, kf[0]);
+        for (;;) {
+            // buffer 0 holds subtile g.  Issue this subtile's key scale first,
+            // then the next subtile's keys, so the scale arrives without
+            // waiting for the prefetch (loads complete in issue order).
+            float ks = 1.f;
+            if (DT == kFP8) ks = k_scale[start + min(key0 + l, L - 1)];
+            const int ga = g + NWV;
+            const int ka = key0 + 64 * NWV;
+            // unconditional (clamped, in bounds): a conditional load would force
+            // the compiler to wait for every outstanding load before using ks
+            I::load_keys_global(kbase, min(ka, L - 1), L - 1, kf[1]);
+            {
+                const float s = I::score(qf, wv, kf[0]) * ks;
+                if (key0 + l < L) scores[start + key0 + l] = s;
+            }
+            g = ga;
+            key0 = ka;
+            if (g >= seg_end) break;
+            if (DT == kFP8) ks = k_scale[start + min(key0 + l, L - 1)];
+            const int gb = g + NWV;
+            const int kbk = key0 + 64 * NWV;
+            I::load_keys_global(kbase, min(kbk, L - 1), L - 1, kf[0]);
+            {
+                const float s = I::score(qf, wv, kf[1]) * ks;
+                if (key0 + l < L) scores[start + key0 + l] = s;
+            }
+            g = gb;
+            key0 = kbk;
+            if (g >= seg_end) break;
         }
-        float s = I::score(qf, wv, kk);
-        const int key = k0 + l;
-        if (DT == kFP8) s *= k_scale[st + min(key, LL - 1)];
-        if (key < LL) scores[st + key] = s;
-    };
-    // two register buffers, alternated by explicit unrolling (no dynamic indexing)
-    for (; g < g1; g += 2 * NWV) {
-        int b1 = 0, k1 = 0, L1 = 0;
-        int64_t s1 = 0;
-        const int ga = g + NWV;
-        if (ga < g1) {
-            locate(ga, b1, k1, L1, s1);
-            I::load_keys_global(kc + (size_t)s1 * I::ROWB, k1, L1 - 1, kf[1]);
-        }
-        finish(b, key0, L, start, kf[0]);
-        if (ga >= g1) break;
-        const int gb = ga + NWV;
-        if (gb < g1) {
-            locate(gb, b, key0, L, start);
-            I::load_keys_global(kc + (size_t)start * I::ROWB, key0, L - 1, kf[0]);
-        }
-        finish(b1, k1, L1, s1, kf[1]);
     }
 }
 

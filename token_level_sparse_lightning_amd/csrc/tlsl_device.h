@@ -76,6 +76,14 @@ struct Mma {
     }
 };
 
+// ReLU as a single v_max_f32.  fmaxf() would also quiet signalling NaNs and
+// costs a second instruction per element; NaN inputs are outside the contract.
+__device__ __forceinline__ float relu(float x) {
+    float y;
+    asm("v_max_f32 %0, 0, %1" : "=v"(y) : "v"(x));
+    return y;
+}
+
 // ---------------------------------------------------------------------------
 // Lightning Indexer epilogue (eq.(1) of the DSA page): for one query, given the
 // per-head dot products of 4 key blocks of 16 keys and the lane's head
