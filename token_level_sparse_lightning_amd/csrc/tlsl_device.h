@@ -76,13 +76,11 @@ struct Mma {
     }
 };
 
-// ReLU as a single v_max_f32.  fmaxf() would also quiet signalling NaNs and
-// costs a second instruction per element; NaN inputs are outside the contract.
-__device__ __forceinline__ float relu(float x) {
-    float y;
-    asm("v_max_f32 %0, 0, %1" : "=v"(y) : "v"(x));
-    return y;
-}
+// ReLU in one integer instruction: a float with the sign bit set is a negative
+// int, so max(bits, 0) maps every negative value (and -0.0) to +0.0 and keeps
+// the rest.  fmaxf() would add a NaN-quieting instruction per element; NaN
+// inputs are outside the contract.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // ---------------------------------------------------------------------------
 // Lightning Indexer epilogue (eq.(1) of the DSA page): for one query, given the
