@@ -3,17 +3,23 @@
 // DSA page, section 1.1 eq.(3): the main attention of query t reads only the
 // entries c_s, s in S_t.  In the weight-absorbed MQA form (section 2) every
 // head reads the same entry, whose full width is the key and whose first Dv
-// components are the value.  One workgroup owns one query row (and, in decode,
-// one slice of its slots); wave w owns heads 16w..16w+15 and keeps their query
-// fragment and their fp32 output accumulator in registers.  Per tile of 32
-// slots the workgroup gathers the selected rows once into LDS, twice laid out:
-//   - row-major [slot][Dqk]  -> A operand of  Z^T = C Q^T  (slots x heads)
-//   - transposed [Dv][slot]  -> A operand of  O^T = V^T P^T (dims x heads)
-// so both products read 16-byte contiguous fragments.  The slot order inside
-// the first product is permuted so that each lane's logits are exactly the
-// P^T fragment the second product needs: the probabilities never leave
-// registers.  Softmax is online (running max and sum per head, base-2
-// exponentials with log2(e) folded into the scale).
+// components are the value.
+//
+// A workgroup owns one query row (decode: one slice of a row's slots) and 16*HBW
+// heads.  Each block of 16 heads belongs to DSPLIT waves that split the work:
+// the logits Z^T = C Q^T over the reduction dims (partial logits are exchanged
+// through LDS) and the output O^T = V^T P^T over the value dims -- so each wave
+// holds part of a query fragment and part of an output accumulator in
+// registers, leaving room to keep the next tile's rows in flight.  Per tile of
+// 32 slots the selected rows are gathered once into LDS, twice laid out:
+// row-major [slot][Dqk] (A operand of Z^T) and transposed [Dv][slot] (A operand
+// of O^T), so both products read 16-byte fragments; the slot order inside the
+// first product is permuted so that each lane's probabilities are exactly the
+// P^T fragment the second product needs.  Softmax is online (running max and
+// sum per head, base-2 exponentials with log2(e) folded into the scale).  When
+// a row needs two head groups, their workgroups are numbered 8 apart so that
+// they run on the same XCD and the second gather of each row is served by that
+// XCD's L2.
 #include <math.h>
 
 #include "tlsl_device.h"
@@ -21,7 +27,8 @@
 
 namespace tlsl {
 
-constexpr int AT_TS = 32;  // slots per tile
+constexpr int AT_TS = 32;      // slots per tile
+constexpr int AT_KMAX = 4096;  // slots per workgroup (k <= 4096)
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -36,6 +43,7 @@ struct AttnArgs {
     const int64_t* cu;        // decode: [B+1]; prefill: null
     int n;                    // prefill sequence length (rows = B*n)
     int H, k, nsplit;
+    int rows;                 // prefill: B*n; decode: B*nsplit
     float scale_log2;         // softmax_scale * log2(e)
     unsigned char* out;       // [rows][H][Dv] (no split) -- dtype of the inputs
     float* lse;               // [rows][H] or null
@@ -43,53 +51,94 @@ struct AttnArgs {
     float* part_ml;           // split: [rows][nsplit][H][2] (running max in log2 units, sum)
 };
 
-template <int DT, int NW, int DQK, int DV, bool DECODE>
-__global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(AttnArgs a) {
+template <int DT, int HBW, int DSPLIT, int DQK, int DV, bool DECODE>
+__global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs a) {
     constexpr int EB = ElemBytes<DT>::v;
+    constexpr int NW = HBW * DSPLIT;
     constexpr int NT = NW * 64;
-    using MQ = Mma<DT, DQK>;
-    using MP = Mma<DT, AT_TS>;
-    constexpr int NCQ = MQ::NCH;
-    constexpr int NCP = MP::NCH;
+    constexpr int HPW = 16 * HBW;             // heads per workgroup
+    constexpr int QKD = DQK / DSPLIT;         // reduction dims per wave
+    constexpr int NCQ = QKD * EB / 64;        // 16-B chunks per lane of the wave's query fragment
+    constexpr int DVW = DV / DSPLIT;          // value dims per wave
+    constexpr int NDB = DVW / 16;             // output dim blocks per wave
+    constexpr int NCP = AT_TS * EB / 64;      // chunks per lane of a P^T / V^T fragment
     constexpr int CROW = DQK * EB;            // bytes of one entry
     constexpr int CSTR = CROW + 16;           // padded LDS row
     constexpr int VROW = AT_TS * EB;          // bytes of one transposed value row
-    constexpr int VSTR = VROW + 16;  // 16-byte aligned rows for the 16-byte fragment reads
+    constexpr int VSTR = VROW + 16;           // 16-byte aligned rows for the 16-byte fragment reads
     constexpr int VPC = 16 / EB;              // values per 16-B chunk
-    constexpr int NDB = DV / 16;              // output dim blocks
-    static_assert(DV % 16 == 0 && DV <= DQK, "value width");
+    static_assert((QKD * EB) % 64 == 0 && DVW % 16 == 0 && DV <= DQK, "shape");
     __shared__ __align__(16) unsigned char ctile[AT_TS * CSTR];
     __shared__ __align__(16) unsigned char vt[DV * VSTR];
-    __shared__ int svalid[AT_TS];
+    __shared__ int slots[AT_KMAX];            // the row's slot range: position or -1
+    __shared__ int tile_any[AT_KMAX / AT_TS];
+    __shared__ int tlist[AT_KMAX / AT_TS];
+    __shared__ int ntl_sh;
+    __shared__ __align__(16) float zx[DSPLIT > 1 ? NT * 8 : 4];  // partial logits of each wave
 
     const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), g = l >> 4, c = l & 15;
-    // which row / slot range
-    int row, split;
+    const int hb = w / DSPLIT, half = w % DSPLIT;
+    // workgroup -> (row, head group); two head groups of a row sit 8 apart
+    const int HG = (a.H + HPW - 1) / HPW;
+    int rs, hgi;
+    if (HG == 1) {
+        rs = blockIdx.x;
+        hgi = 0;
+    } else {
+        const int grp = blockIdx.x / (8 * HG), rem = blockIdx.x % (8 * HG);
+        hgi = rem / 8;
+        rs = grp * 8 + rem % 8;
+    }
+    if (rs >= a.rows) return;
+    int qrow, split;
     int64_t kv_base;
     int limit;
     if constexpr (DECODE) {
-        row = blockIdx.x / a.nsplit;
-        split = blockIdx.x % a.nsplit;
-        kv_base = a.cu[row];
-        limit = (int)(a.cu[row + 1] - kv_base) - 1;
+        qrow = rs / a.nsplit;
+        split = rs % a.nsplit;
+        kv_base = a.cu[qrow];
+        limit = (int)(a.cu[qrow + 1] - kv_base) - 1;
     } else {
-        row = blockIdx.x;
+        qrow = rs;
         split = 0;
-        const int b = row / a.n;
+        const int b = qrow / a.n;
         kv_base = (int64_t)b * a.n;
-        limit = row - b * a.n;
+        limit = qrow - b * a.n;
     }
     const int per = (a.k + a.nsplit - 1) / a.nsplit;
     const int sbeg = split * per;
     const int send = min(a.k, sbeg + per);
-    const int32_t* Srow = a.S + (size_t)row * a.k;
+    const int nsl = max(send - sbeg, 0);
+    const int ntiles = (nsl + AT_TS - 1) / AT_TS;
+    const int32_t* Srow = a.S + (size_t)qrow * a.k;
 
-    // query fragment (B operand of Z^T = C Q^T): column = head 16w + c
-    const int h = 16 * w + c;
+    // the row's slot range, staged once: valid position or -1, padded to whole
+    // tiles; tiles without a valid slot are skipped
+    for (int i = tid; i < ntiles * AT_TS; i += NT) {
+        const int pos = i < nsl ? Srow[sbeg + i] : -1;
+        slots[i] = (pos >= 0 && pos <= limit) ? pos : -1;
+    }
+    for (int i = tid; i < ntiles; i += NT) tile_any[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < ntiles * AT_TS; i += NT)
+        if (slots[i] >= 0) tile_any[i / AT_TS] = 1;
+    __syncthreads();
+    if (tid == 0) {
+        int m = 0;
+        for (int i = 0; i < ntiles; ++i)
+            if (tile_any[i]) tlist[m++] = i;
+        ntl_sh = m;
+    }
+
+    // query fragment (B operand of Z^T = C Q^T): column = head h, this wave's
+    // share of the reduction dims
+    const int h = hgi * HPW + 16 * hb + c;
     const bool hvalid = h < a.H;
+    const int kd0 = half * QKD;  // first reduction dim of this wave
     uint4 qf[NCQ];
     {
-        const uint4* src = reinterpret_cast<const uint4*>(a.q + ((size_t)row * a.H + (hvalid ? h : 0)) * CROW + g * (CROW / 4));
+        const uint4* src = reinterpret_cast<const uint4*>(a.q + ((size_t)qrow * a.H + (hvalid ? h : 0)) * CROW +
+                                                          (kd0 + g * (QKD / 4)) * EB);
 #pragma unroll
         for (int ch = 0; ch < NCQ; ++ch) qf[ch] = hvalid ? src[ch] : make_uint4(0, 0, 0, 0);
     }
@@ -97,76 +146,132 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
+    __syncthreads();
+    const int ntl = ntl_sh;
 
-    for (int s0 = sbeg; s0 < send; s0 += AT_TS) {
-        // ---- gather the tile ------------------------------------------------
-        __syncthreads();
-        int my_valid = 0;
-        if (tid < AT_TS) {
-            const int si = s0 + tid;
-            const int pos = si < send ? Srow[si] : -1;
-            my_valid = (pos >= 0 && pos <= limit) ? 1 : 0;
-            svalid[tid] = my_valid ? pos : -1;
-        }
-        if (!__syncthreads_or(my_valid)) continue;
-        // value part: item = (slot quad, chunk of VPC dims); row-major and transposed
-        // slot quad varies fastest across lanes: the transposed writes of one
-        // instruction then cover 8 rows x 8 quads, spread over all banks
-        for (int it = tid; it < (AT_TS / 4) * (DV / VPC); it += NT) {
-            const int qd = it % (AT_TS / 4), oc = it / (AT_TS / 4);
-            uint4 v[4];
+    // ---- gather of one tile: value part (quad of slots x 16-byte chunk) and
+    // position part (row x chunk); registers first, LDS after the compute ----
+    constexpr int VITEMS = (AT_TS / 4) * (DV / VPC);
+    constexpr int VPER = (VITEMS + NT - 1) / NT;
+    constexpr int RC = (DQK - DV) / VPC;  // position-part chunks per row
+    constexpr int RITEMS = AT_TS * RC;
+    constexpr int RPER = (RITEMS + NT - 1) / NT;
+    uint4 pv[VPER][4];
+    uint4 pr[RPER > 0 ? RPER : 1];
+    auto load_tile = [&](int t) {
+        const int* sl = slots + t * AT_TS;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int pos = svalid[4 * qd + u];
-                v[u] = pos >= 0 ? *reinterpret_cast<const uint4*>(a.kv + (size_t)(kv_base + pos) * CROW + oc * 16)
-                                : make_uint4(0, 0, 0, 0);
-                *reinterpret_cast<uint4*>(ctile + (4 * qd + u) * CSTR + oc * 16) = v[u];
-            }
-            if constexpr (EB == 2) {
-                const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&v[0]);
-                const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&v[1]);
-                const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&v[2]);
-                const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&v[3]);
+        for (int j = 0; j < VPER; ++j) {
+            const int it = tid + j * NT;
+            if (it < VITEMS) {
+                // slot quad varies fastest across lanes (spreads the transposed writes)
+                const int qd = it % (AT_TS / 4), oc = it / (AT_TS / 4);
 #pragma unroll
-                for (int i = 0; i < VPC; ++i) {
-                    uint2 pk = make_uint2((uint32_t)e0[i] | ((uint32_t)e1[i] << 16), (uint32_t)e2[i] | ((uint32_t)e3[i] << 16));
-                    *reinterpret_cast<uint2*>(vt + (oc * VPC + i) * VSTR + 4 * qd * EB) = pk;
+                for (int u = 0; u < 4; ++u) {
+                    const int pos = sl[4 * qd + u];
+                    pv[j][u] = pos >= 0 ? *reinterpret_cast<const uint4*>(a.kv + (size_t)(kv_base + pos) * CROW + oc * 16)
+                                        : make_uint4(0, 0, 0, 0);
                 }
-            } else {
-                const uint32_t* e0 = reinterpret_cast<const uint32_t*>(&v[0]);
-                const uint32_t* e1 = reinterpret_cast<const uint32_t*>(&v[1]);
-                const uint32_t* e2 = reinterpret_cast<const uint32_t*>(&v[2]);
-                const uint32_t* e3 = reinterpret_cast<const uint32_t*>(&v[3]);
-#pragma unroll
-                for (int i = 0; i < VPC; ++i)
-                    *reinterpret_cast<uint4*>(vt + (oc * VPC + i) * VSTR + 4 * qd * EB) = make_uint4(e0[i], e1[i], e2[i], e3[i]);
             }
         }
-        // position part (dims DV..DQK-1): row-major only
-        constexpr int RC = (DQK - DV) / VPC;  // chunks per row
-        for (int it = tid; it < AT_TS * RC; it += NT) {
-            const int r = it / RC, oc = DV / VPC + it % RC;
-            const int pos = svalid[r];
-            *reinterpret_cast<uint4*>(ctile + r * CSTR + oc * 16) =
-                pos >= 0 ? *reinterpret_cast<const uint4*>(a.kv + (size_t)(kv_base + pos) * CROW + oc * 16)
-                         : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < RPER; ++j) {
+            const int it = tid + j * NT;
+            if (it < RITEMS) {
+                const int r = it / RC, oc = DV / VPC + it % RC;
+                const int pos = sl[r];
+                pr[j] = pos >= 0 ? *reinterpret_cast<const uint4*>(a.kv + (size_t)(kv_base + pos) * CROW + oc * 16)
+                                 : make_uint4(0, 0, 0, 0);
+            }
         }
-        __syncthreads();
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int j = 0; j < VPER; ++j) {
+            const int it = tid + j * NT;
+            if (it < VITEMS) {
+                const int qd = it % (AT_TS / 4), oc = it / (AT_TS / 4);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(ctile + (4 * qd + u) * CSTR + oc * 16) = pv[j][u];
+                if constexpr (EB == 2) {
+                    const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&pv[j][0]);
+                    const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&pv[j][1]);
+                    const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&pv[j][2]);
+                    const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&pv[j][3]);
+#pragma unroll
+                    for (int i = 0; i < VPC; ++i) {
+                        uint2 pk = make_uint2((uint32_t)e0[i] | ((uint32_t)e1[i] << 16), (uint32_t)e2[i] | ((uint32_t)e3[i] << 16));
+                        *reinterpret_cast<uint2*>(vt + (oc * VPC + i) * VSTR + 4 * qd * EB) = pk;
+                    }
+                } else {
+                    const uint32_t* e0 = reinterpret_cast<const uint32_t*>(&pv[j][0]);
+                    const uint32_t* e1 = reinterpret_cast<const uint32_t*>(&pv[j][1]);
+                    const uint32_t* e2 = reinterpret_cast<const uint32_t*>(&pv[j][2]);
+                    const uint32_t* e3 = reinterpret_cast<const uint32_t*>(&pv[j][3]);
+#pragma unroll
+                    for (int i = 0; i < VPC; ++i)
+                        *reinterpret_cast<uint4*>(vt + (oc * VPC + i) * VSTR + 4 * qd * EB) = make_uint4(e0[i], e1[i], e2[i], e3[i]);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RPER; ++j) {
+            const int it = tid + j * NT;
+            if (it < RITEMS) {
+                const int r = it / RC, oc = DV / VPC + it % RC;
+                *reinterpret_cast<uint4*>(ctile + r * CSTR + oc * 16) = pr[j];
+            }
+        }
+    };
+    // one 16-byte chunk of the reduction dimension through the matrix cores
+    auto mma_chunk = [](const uint4& x, const uint4& y, v4f acc) -> v4f {
+        if constexpr (DT == kBF16) {
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, x), __builtin_bit_cast(v8bf, y), acc, 0, 0, 0);
+        } else {
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(x.x), __uint_as_float(y.x), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(x.y), __uint_as_float(y.y), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(x.z), __uint_as_float(y.z), acc, 0, 0, 0);
+            return __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(x.w), __uint_as_float(y.w), acc, 0, 0, 0);
+        }
+    };
+
+    if (ntl > 0) {
+        load_tile(tlist[0]);
+        store_tile();
+    }
+    __syncthreads();
+    for (int ti = 0; ti < ntl; ++ti) {
+        const int tcur = tlist[ti];
+        // the next tile's rows travel while this one is computed
+        if (ti + 1 < ntl) load_tile(tlist[ti + 1]);
+        const int* sl = slots + tcur * AT_TS;
 
         // ---- logits: Z^T[slot][head]; lane (g,c) gets slots 8g..8g+7 of head c
         float z[8];
+        {
+            const uint4* cp0 = reinterpret_cast<const uint4*>(ctile + (8 * (c >> 2) + (c & 3)) * CSTR + (kd0 + g * (QKD / 4)) * EB);
+            const uint4* cp1 = reinterpret_cast<const uint4*>(ctile + (8 * (c >> 2) + 4 + (c & 3)) * CSTR + (kd0 + g * (QKD / 4)) * EB);
+            v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            const int slot_row = 8 * (c >> 2) + 4 * sb + (c & 3);
-            const uint4* cp = reinterpret_cast<const uint4*>(ctile + slot_row * CSTR + g * (CROW / 4));
-            uint4 cf[NCQ];
-#pragma unroll
-            for (int ch = 0; ch < NCQ; ++ch) cf[ch] = cp[ch];
-            const v4f acc = MQ::run(cf, qf, v4f{0.f, 0.f, 0.f, 0.f});
+            for (int ch = 0; ch < NCQ; ++ch) {
+                acc0 = mma_chunk(cp0[ch], qf[ch], acc0);
+                acc1 = mma_chunk(cp1[ch], qf[ch], acc1);
+            }
+            if constexpr (DSPLIT > 1) {
+                // add the partner wave's partial logits (the same sum in both waves)
+                float4* mine = reinterpret_cast<float4*>(zx + (size_t)tid * 8);
+                mine[0] = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
+                mine[1] = make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
+                __syncthreads();
+                const float4* oth = reinterpret_cast<const float4*>(zx + (size_t)(tid ^ 64) * 8);
+                const float4 o0 = oth[0], o1 = oth[1];
+                acc0[0] += o0.x; acc0[1] += o0.y; acc0[2] += o0.z; acc0[3] += o0.w;
+                acc1[0] += o1.x; acc1[1] += o1.y; acc1[2] += o1.z; acc1[3] += o1.w;
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int slot = 8 * g + 4 * sb + r;
-                z[4 * sb + r] = svalid[slot] >= 0 ? acc[r] * a.scale_log2 : -INFINITY;
+                z[r] = sl[8 * g + r] >= 0 ? acc0[r] * a.scale_log2 : -INFINITY;
+                z[4 + r] = sl[8 * g + 4 + r] >= 0 ? acc1[r] * a.scale_log2 : -INFINITY;
             }
         }
         // ---- online softmax per head -----------------------------------------
@@ -210,35 +315,34 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(AttnArgs a) {
         // ---- O^T[d][head] += V^T[d][slots] P^T[slots][head] -------------------
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            const uint4* vp = reinterpret_cast<const uint4*>(vt + (16 * db + c) * VSTR + g * (VROW / 4));
-            uint4 vf[NCP];
+            const uint4* vp = reinterpret_cast<const uint4*>(vt + (half * DVW + 16 * db + c) * VSTR + g * (VROW / 4));
 #pragma unroll
-            for (int ch = 0; ch < NCP; ++ch) vf[ch] = vp[ch];
-            o[db] = MP::run(vf, pf, o[db]);
+            for (int ch = 0; ch < NCP; ++ch) o[db] = mma_chunk(vp[ch], pf[ch], o[db]);
         }
+        __syncthreads();
+        if (ti + 1 < ntl) store_tile();
+        __syncthreads();
     }
 
     // ---- finish --------------------------------------------------------------
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
+    if (!hvalid) return;
     if (a.part_o) {
-        // split: unnormalised partials
-        const size_t pidx = ((size_t)row * a.nsplit + split) * a.H + h;
-        if (hvalid) {
-            float* po = a.part_o + pidx * DV;
+        // split: unnormalised partials of this wave's value dims
+        const size_t pidx = (size_t)rs * a.H + h;
+        float* po = a.part_o + pidx * DV + half * DVW;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                *reinterpret_cast<float4*>(po + 16 * db + 4 * g) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
-            if (g == 0) {
-                a.part_ml[pidx * 2] = m_run;
-                a.part_ml[pidx * 2 + 1] = l_tot;
-            }
+        for (int db = 0; db < NDB; ++db)
+            *reinterpret_cast<float4*>(po + 16 * db + 4 * g) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
+        if (g == 0 && half == 0) {
+            a.part_ml[pidx * 2] = m_run;
+            a.part_ml[pidx * 2 + 1] = l_tot;
         }
         return;
     }
-    if (!hvalid) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    unsigned char* op = a.out + ((size_t)row * a.H + h) * DV * EB;
+    unsigned char* op = a.out + (((size_t)qrow * a.H + h) * DV + half * DVW) * EB;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
         const int d0 = 16 * db + 4 * g;
@@ -250,8 +354,8 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(AttnArgs a) {
             *reinterpret_cast<float4*>(op + d0 * 4) = make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
         }
     }
-    if (a.lse && g == 0)
-        a.lse[(size_t)row * a.H + h] = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+    if (a.lse && g == 0 && half == 0)
+        a.lse[(size_t)qrow * a.H + h] = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
 }
 
 // Merge the split partials of a decode row: o = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s.
@@ -304,33 +408,41 @@ bool attn_supported(const AttnShape& s) {
     return false;
 }
 
-static int decode_splits(int B, int k) {
-    int ns = (256 + B - 1) / B;
+// Slot splits per decode row: about one workgroup per CU over the batch's rows
+// and head groups, at least 128 slots per split.
+static int decode_splits(const AttnShape& s, int B, int k) {
+    const int hpw = s.dt == kBF16 ? 64 : 16;
+    const int hg = (s.H + hpw - 1) / hpw;
+    const int cus = device_cu_count();
+    int ns = (cus + B * hg - 1) / (B * hg);
     const int maxs = (k + 127) / 128;
     if (ns > maxs) ns = maxs;
     return ns < 1 ? 1 : ns;
 }
 
 size_t attn_decode_ws_bytes(const AttnShape& s, int B, int k) {
-    const int ns = decode_splits(B, k);
+    const int ns = decode_splits(s, B, k);
     if (ns == 1) return 256;  // never empty, so that a NULL workspace always means "size query"
     const size_t parts = (size_t)B * ns * s.H;
     return parts * s.Dv * sizeof(float) + ((parts * 2 * sizeof(float) + 255) & ~(size_t)255) + 256;
 }
 
-template <int DT, int NW, int DQK, int DV, bool DEC>
-static void launch_attn_t(const AttnArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((sparse_attn_kernel<DT, NW, DQK, DV, DEC>), dim3(grid), dim3(NW * 64), 0, st, a);
+template <int DT, int HBW, int DSPLIT, int DQK, int DV, bool DEC>
+static void launch_attn_t(AttnArgs a, int rows, hipStream_t st) {
+    constexpr int HPW = 16 * HBW;
+    const int hg = (a.H + HPW - 1) / HPW;
+    a.rows = rows;
+    const int grid = hg == 1 ? rows : (rows + 7) / 8 * 8 * hg;
+    hipLaunchKernelGGL((sparse_attn_kernel<DT, HBW, DSPLIT, DQK, DV, DEC>), dim3(grid), dim3(HBW * DSPLIT * 64), 0, st,
+                       a);
 }
 
 template <bool DEC>
-static void dispatch_attn(const AttnShape& s, const AttnArgs& a, int grid, hipStream_t st) {
-    if (s.dt == kBF16) {
-        if (s.H <= 16) launch_attn_t<kBF16, 1, 576, 512, DEC>(a, grid, st);
-        else launch_attn_t<kBF16, 8, 576, 512, DEC>(a, grid, st);
-    } else {
-        launch_attn_t<kF32, 1, 80, 64, DEC>(a, grid, st);
-    }
+static void dispatch_attn(const AttnShape& s, const AttnArgs& a, int rows, hipStream_t st) {
+    if (s.dt == kBF16)
+        launch_attn_t<kBF16, 4, 2, 576, 512, DEC>(a, rows, st);
+    else
+        launch_attn_t<kF32, 1, 1, 80, 64, DEC>(a, rows, st);
 }
 
 hipError_t launch_sparse_attn_prefill(const AttnShape& s, const void* q, const void* kv, const int32_t* S, int B,
@@ -354,7 +466,7 @@ hipError_t launch_sparse_attn_prefill(const AttnShape& s, const void* q, const v
 hipError_t launch_sparse_attn_decode(const AttnShape& s, const void* q, const void* kv, const int64_t* cu,
                                      const int32_t* S, int B, int k, float scale, void* out, float* lse, void* ws,
                                      hipStream_t st) {
-    const int ns = decode_splits(B, k);
+    const int ns = decode_splits(s, B, k);
     AttnArgs a{};
     a.q = static_cast<const unsigned char*>(q);
     a.kv = static_cast<const unsigned char*>(kv);

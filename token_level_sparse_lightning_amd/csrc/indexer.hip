@@ -645,7 +645,7 @@ __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned cha
 // Host launchers.
 // ---------------------------------------------------------------------------
 // Compute units of the current device (queried once per device).
-static int device_cu_count() {
+int device_cu_count() {
     static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

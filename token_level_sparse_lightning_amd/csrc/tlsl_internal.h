@@ -8,6 +8,9 @@
 
 namespace tlsl {
 
+// Compute units of the current device (queried once per device).
+int device_cu_count();
+
 // ---- indexer ---------------------------------------------------------------
 struct IndexerShape {
     int dt;      // 0 f32, 1 bf16, 2 fp8
