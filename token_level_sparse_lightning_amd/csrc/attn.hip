@@ -68,13 +68,18 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     constexpr int VSTR = VROW + 16;           // 16-byte aligned rows for the 16-byte fragment reads
     constexpr int VPC = 16 / EB;              // values per 16-B chunk
     static_assert((QKD * EB) % 64 == 0 && DVW % 16 == 0 && DV <= DQK, "shape");
-    __shared__ __align__(16) unsigned char ctile[AT_TS * CSTR];
+    auto crow = [](int r) { return r * CSTR + (r >> 4) * 64; };
+    // rows 16 apart are shifted by 64 bytes so that the 16 rows one lane
+    // group reads for the logits fall in distinct banks
+    __shared__ __align__(16) unsigned char ctile[AT_TS * CSTR + (AT_TS / 16) * 64];
     __shared__ __align__(16) unsigned char vt[DV * VSTR];
     __shared__ int slots[AT_KMAX];            // the row's slot range: position or -1
     __shared__ int tile_any[AT_KMAX / AT_TS];
     __shared__ int tlist[AT_KMAX / AT_TS];
     __shared__ int ntl_sh;
-    __shared__ __align__(16) float zx[DSPLIT > 1 ? NT * 8 : 4];  // partial logits of each wave
+    // partial logits of each wave, lane-contiguous (conflict-free exchange)
+    __shared__ __align__(16) float4 zx0[DSPLIT > 1 ? NT : 1];
+    __shared__ __align__(16) float4 zx1[DSPLIT > 1 ? NT : 1];
 
     const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), g = l >> 4, c = l & 15;
     const int hb = w / DSPLIT, half = w % DSPLIT;
@@ -156,58 +161,62 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     constexpr int RC = (DQK - DV) / VPC;  // position-part chunks per row
     constexpr int RITEMS = AT_TS * RC;
     constexpr int RPER = (RITEMS + NT - 1) / NT;
-    uint4 pv[VPER][4];
-    uint4 pr[RPER > 0 ? RPER : 1];
-    auto load_tile = [&](int t) {
+    struct Pre {
+        uint4 v[VPER][4];
+        uint4 r[RPER > 0 ? RPER : 1];
+    };
+    auto load_tile = [&](int t, Pre& P) {
         const int* sl = slots + t * AT_TS;
+        // every thread issues the same loads (items past the end repeat the
+        // last one) so that the compiler's wait counts stay exact
 #pragma unroll
         for (int j = 0; j < VPER; ++j) {
-            const int it = tid + j * NT;
-            if (it < VITEMS) {
+            const int it = min(tid + j * NT, VITEMS - 1);
+            {
                 // slot quad varies fastest across lanes (spreads the transposed writes)
                 const int qd = it % (AT_TS / 4), oc = it / (AT_TS / 4);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const int pos = sl[4 * qd + u];
-                    pv[j][u] = pos >= 0 ? *reinterpret_cast<const uint4*>(a.kv + (size_t)(kv_base + pos) * CROW + oc * 16)
-                                        : make_uint4(0, 0, 0, 0);
+                    // an invalid slot reads the row's entry 0 (always in bounds):
+                    // its logit is masked to -inf, so its probability is exactly 0
+                    const int pos = max(sl[4 * qd + u], 0);
+                    P.v[j][u] = *reinterpret_cast<const uint4*>(a.kv + (size_t)(kv_base + pos) * CROW + oc * 16);
                 }
             }
         }
 #pragma unroll
         for (int j = 0; j < RPER; ++j) {
-            const int it = tid + j * NT;
-            if (it < RITEMS) {
+            const int it = min(tid + j * NT, RITEMS - 1);
+            {
                 const int r = it / RC, oc = DV / VPC + it % RC;
-                const int pos = sl[r];
-                pr[j] = pos >= 0 ? *reinterpret_cast<const uint4*>(a.kv + (size_t)(kv_base + pos) * CROW + oc * 16)
-                                 : make_uint4(0, 0, 0, 0);
+                const int pos = max(sl[r], 0);
+                P.r[j] = *reinterpret_cast<const uint4*>(a.kv + (size_t)(kv_base + pos) * CROW + oc * 16);
             }
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](const Pre& P) {
 #pragma unroll
         for (int j = 0; j < VPER; ++j) {
             const int it = tid + j * NT;
             if (it < VITEMS) {
                 const int qd = it % (AT_TS / 4), oc = it / (AT_TS / 4);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(ctile + (4 * qd + u) * CSTR + oc * 16) = pv[j][u];
+                for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(ctile + crow(4 * qd + u) + oc * 16) = P.v[j][u];
                 if constexpr (EB == 2) {
-                    const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&pv[j][0]);
-                    const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&pv[j][1]);
-                    const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&pv[j][2]);
-                    const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&pv[j][3]);
+                    const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&P.v[j][0]);
+                    const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&P.v[j][1]);
+                    const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&P.v[j][2]);
+                    const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&P.v[j][3]);
 #pragma unroll
                     for (int i = 0; i < VPC; ++i) {
                         uint2 pk = make_uint2((uint32_t)e0[i] | ((uint32_t)e1[i] << 16), (uint32_t)e2[i] | ((uint32_t)e3[i] << 16));
                         *reinterpret_cast<uint2*>(vt + (oc * VPC + i) * VSTR + 4 * qd * EB) = pk;
                     }
                 } else {
-                    const uint32_t* e0 = reinterpret_cast<const uint32_t*>(&pv[j][0]);
-                    const uint32_t* e1 = reinterpret_cast<const uint32_t*>(&pv[j][1]);
-                    const uint32_t* e2 = reinterpret_cast<const uint32_t*>(&pv[j][2]);
-                    const uint32_t* e3 = reinterpret_cast<const uint32_t*>(&pv[j][3]);
+                    const uint32_t* e0 = reinterpret_cast<const uint32_t*>(&P.v[j][0]);
+                    const uint32_t* e1 = reinterpret_cast<const uint32_t*>(&P.v[j][1]);
+                    const uint32_t* e2 = reinterpret_cast<const uint32_t*>(&P.v[j][2]);
+                    const uint32_t* e3 = reinterpret_cast<const uint32_t*>(&P.v[j][3]);
 #pragma unroll
                     for (int i = 0; i < VPC; ++i)
                         *reinterpret_cast<uint4*>(vt + (oc * VPC + i) * VSTR + 4 * qd * EB) = make_uint4(e0[i], e1[i], e2[i], e3[i]);
@@ -219,7 +228,7 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             const int it = tid + j * NT;
             if (it < RITEMS) {
                 const int r = it / RC, oc = DV / VPC + it % RC;
-                *reinterpret_cast<uint4*>(ctile + r * CSTR + oc * 16) = pr[j];
+                *reinterpret_cast<uint4*>(ctile + crow(r) + oc * 16) = P.r[j];
             }
         }
     };
@@ -235,22 +244,17 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
         }
     };
 
-    if (ntl > 0) {
-        load_tile(tlist[0]);
-        store_tile();
-    }
-    __syncthreads();
-    for (int ti = 0; ti < ntl; ++ti) {
-        const int tcur = tlist[ti];
-        // the next tile's rows travel while this one is computed
-        if (ti + 1 < ntl) load_tile(tlist[ti + 1]);
+    // the tile being computed sits in LDS while the next one is in flight into
+    // registers (loads are unconditional -- past the end they repeat the last
+    // tile -- so the compiler's wait counts stay exact)
+    auto compute = [&](int tcur) {
         const int* sl = slots + tcur * AT_TS;
 
         // ---- logits: Z^T[slot][head]; lane (g,c) gets slots 8g..8g+7 of head c
         float z[8];
         {
-            const uint4* cp0 = reinterpret_cast<const uint4*>(ctile + (8 * (c >> 2) + (c & 3)) * CSTR + (kd0 + g * (QKD / 4)) * EB);
-            const uint4* cp1 = reinterpret_cast<const uint4*>(ctile + (8 * (c >> 2) + 4 + (c & 3)) * CSTR + (kd0 + g * (QKD / 4)) * EB);
+            const uint4* cp0 = reinterpret_cast<const uint4*>(ctile + crow(8 * (c >> 2) + (c & 3)) + (kd0 + g * (QKD / 4)) * EB);
+            const uint4* cp1 = reinterpret_cast<const uint4*>(ctile + crow(8 * (c >> 2) + 4 + (c & 3)) + (kd0 + g * (QKD / 4)) * EB);
             v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ch = 0; ch < NCQ; ++ch) {
@@ -259,12 +263,10 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             }
             if constexpr (DSPLIT > 1) {
                 // add the partner wave's partial logits (the same sum in both waves)
-                float4* mine = reinterpret_cast<float4*>(zx + (size_t)tid * 8);
-                mine[0] = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
-                mine[1] = make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
+                zx0[tid] = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
+                zx1[tid] = make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
                 __syncthreads();
-                const float4* oth = reinterpret_cast<const float4*>(zx + (size_t)(tid ^ 64) * 8);
-                const float4 o0 = oth[0], o1 = oth[1];
+                const float4 o0 = zx0[tid ^ 64], o1 = zx1[tid ^ 64];
                 acc0[0] += o0.x; acc0[1] += o0.y; acc0[2] += o0.z; acc0[3] += o0.w;
                 acc1[0] += o1.x; acc1[1] += o1.y; acc1[2] += o1.z; acc1[3] += o1.w;
             }
@@ -319,8 +321,20 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
 #pragma unroll
             for (int ch = 0; ch < NCP; ++ch) o[db] = mma_chunk(vp[ch], pf[ch], o[db]);
         }
+    };
+    Pre P;
+    if (ntl > 0) {
+        load_tile(tlist[0], P);
+        store_tile(P);
+    }
+    __syncthreads();
+    for (int ti = 0; ti < ntl; ++ti) {
+        load_tile(tlist[min(ti + 1, ntl - 1)], P);
+        asm volatile("" ::: "memory");
+        compute(tlist[ti]);
         __syncthreads();
-        if (ti + 1 < ntl) store_tile();
+        if (ti + 1 >= ntl) break;
+        store_tile(P);
         __syncthreads();
     }
 

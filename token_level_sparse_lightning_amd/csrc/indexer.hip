@@ -83,6 +83,13 @@ struct Idx {
                 for (int r = 0; r < 4; ++r) p = __builtin_fmaf(wv[hb][r], relu(acc[hb][r]), p);
             part[kb] = p;
         }
+        // interleave matrix-core and vector work (1 product : 8 vector ops) so
+        // that one wave's epilogue overlaps its next products
+#pragma unroll
+        for (int i = 0; i < 4 * HB * (DT == kF32 ? 4 * NCH : (DT == kBF16 ? NCH : NCH / 2)); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
         return reduce_heads_64(part);
     }
 
