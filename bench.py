@@ -14,9 +14,14 @@ rows of the path measured on their own workloads:
                 index_decode + topk_select + sparse_attn_decode, tokens/s
 
 Timing: W untimed warm-up calls, then exactly K calls between two device
-synchronisations (wall clock), plus HIP events on the launch stream around
-every timed call (the kernel time the roofline uses).  Inputs are resident in
-HBM before the timed region; workspaces are allocated once outside it.
+synchronisations (wall clock; `value` and ms_per_step use it), with HIP
+events on the launch stream around every timed call (median and minimum
+reported) and, through the library's kernel timer, HIP events on the same
+stream around every launch of the workload's main kernel: the roofline of
+the headline uses prefill_score_kernel's average launch time.  Inputs are
+resident in HBM before the timed region; workspaces are allocated once
+outside it.  A calibration leg measures a 1 GiB streaming copy and dense
+bf16 / fp8 matrix-core loops on the same device.
 
 The CPU baseline times the oracle (test infrastructure, double precision) on
 a bounded sample of query rows of the headline workload.
@@ -49,13 +54,34 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def time_calls(fn, steps, warmup):
-    """Returns (wall ms per call, event ms per call)."""
+class Timing:
+    """Wall and event times of K timed calls (ms per call)."""
+
+    def __init__(self, wall, ev, kern):
+        self.wall = wall
+        self.ev_med = float(np.median(ev))
+        self.ev_min = float(np.min(ev))
+        self.kernel_launches, tot, self.kernel_min, self.kernel_max = kern if kern else (0, 0.0, 0.0, 0.0)
+        self.kernel_avg = tot / self.kernel_launches if self.kernel_launches else None
+
+    def as_dict(self):
+        d = dict(ms_per_call=self.wall, event_ms_median=self.ev_med, event_ms_min=self.ev_min)
+        if self.kernel_launches:
+            d.update(kernel_ms_avg=self.kernel_avg, kernel_ms_min=self.kernel_min, kernel_launches=self.kernel_launches)
+        return d
+
+
+def time_calls(fn, steps, warmup, kernel=None):
+    """W untimed calls, then K calls between two synchronisations.  HIP events
+    on the launch stream bracket every call; when ``kernel`` is named, the
+    library also brackets each launch of that kernel with its own events."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    if kernel:
+        tl.timer_arm(kernel, max_launches=8 * steps)
     t0 = time.perf_counter()
     for a, b in evs:
         a.record(st)
@@ -63,8 +89,8 @@ def time_calls(fn, steps, warmup):
         b.record(st)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    ev = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    return wall, ev
+    kern = tl.timer_collect() if kernel else None
+    return Timing(wall, [a.elapsed_time(b) for a, b in evs], kern)
 
 
 def causal_pairs(B, n):
@@ -84,12 +110,15 @@ def bench_prefill(n, dt, seed, steps, warmup, plant_max_dist=None):
     def call():
         tl.index_prefill(inp.q, inp.k, inp.w, k, q_scale=inp.q_scale, k_scale=inp.k_scale, S=S, workspace=ws)
 
-    wall, ev = time_calls(call, steps, warmup)
+    tm = time_calls(call, steps, warmup, kernel="prefill_score_kernel")
     pairs = causal_pairs(1, n)
     flops = 2.0 * HI * DI * pairs
     peak = PEAK_FP8_TFLOPS if dt == synth.DT_FP8 else PEAK_BF16_TFLOPS
-    ach = flops / (ev * 1e-3) / 1e12
-    log(f"prefill n={n}: {ev:.3f} ms/call (events), {wall:.3f} ms (wall), {ach:.1f} TFLOP/s")
+    call_tf = flops / (tm.ev_med * 1e-3) / 1e12
+    kern_tf = flops / (tm.kernel_avg * 1e-3) / 1e12
+    log(f"prefill n={n}: {tm.ev_med:.3f} ms/call (events, median; min {tm.ev_min:.3f}), {tm.wall:.3f} ms (wall), "
+        f"{call_tf:.1f} TFLOP/s per call; prefill_score_kernel {tm.kernel_avg:.3f} ms avg over "
+        f"{tm.kernel_launches} launches = {kern_tf:.1f} TFLOP/s")
     probes = inp.probes
     recall = None
     if probes:
@@ -100,11 +129,16 @@ def bench_prefill(n, dt, seed, steps, warmup, plant_max_dist=None):
             hit += sum(p in sel for p in pos)
             tot += len(pos)
         recall = hit / max(tot, 1)
+    # algorithmic bytes of one call: Q^I, K^I, W^I and scales read once, S written once
+    eb = 1 if dt == synth.DT_FP8 else (2 if dt == synth.DT_BF16 else 4)
+    scale_b = 8 * n if dt == synth.DT_FP8 else 0
+    nbytes = n * HI * DI * eb + n * DI * eb + n * HI * 4 + scale_b + n * k * 4
     res = dict(workload=f"prefill indexer + top-k: B=1, n={n}, H^I={HI}, d^I={DI}, k={k}, "
                         f"{synth.DT_NAMES[dt]}, planted keys",
-               pairs_per_s=pairs / (wall * 1e-3), ms_per_call=wall, kernel_ms=ev, pairs=pairs,
-               flops_per_call=flops, achieved_tflops=ach, peak_tflops=peak, frac=ach / peak,
-               planted_recall=recall)
+               pairs_per_s=pairs / (tm.wall * 1e-3), pairs=pairs, flops_per_call=flops,
+               call_tflops=call_tf, kernel="prefill_score_kernel", kernel_tflops=kern_tf, peak_tflops=peak,
+               frac=kern_tf / peak, call_frac=call_tf / peak, algorithmic_bytes_per_call=nbytes,
+               planted_recall=recall, **tm.as_dict())
     return res, inp, S
 
 
@@ -118,15 +152,16 @@ def bench_attn_prefill(S, n, seed, steps, warmup):
     def call():
         tl.sparse_attn_prefill(q, kv, S, scale, Dv, out=out)
 
-    wall, ev = time_calls(call, steps, warmup)
+    tm = time_calls(call, steps, warmup, kernel="sparse_attn_kernel")
     valid = int((S >= 0).sum().item())
     flops = 2.0 * H * (Dqk + Dv) * valid
-    ach = flops / (ev * 1e-3) / 1e12
-    log(f"attn prefill: {ev:.3f} ms/call, {ach:.1f} TFLOP/s")
+    ach = flops / (tm.kernel_avg * 1e-3) / 1e12
+    log(f"attn prefill: {tm.ev_med:.3f} ms/call (events, median), sparse_attn_kernel {tm.kernel_avg:.3f} ms, "
+        f"{ach:.1f} TFLOP/s")
     del q, kv, out
     return dict(workload=f"sparse attention prefill: n={n}, H={H}, Dqk={Dqk}, Dv={Dv}, k=2048, bf16",
-                ms_per_call=wall, kernel_ms=ev, valid_slots=valid, flops_per_call=flops,
-                achieved_tflops=ach, peak_tflops=PEAK_BF16_TFLOPS, frac=ach / PEAK_BF16_TFLOPS)
+                valid_slots=valid, flops_per_call=flops, kernel="sparse_attn_kernel", kernel_tflops=ach,
+                peak_tflops=PEAK_BF16_TFLOPS, frac=ach / PEAK_BF16_TFLOPS, **tm.as_dict())
 
 
 def decode_bytes(lengths, HI, DI, H, Dqk, Dv, k):
@@ -135,6 +170,22 @@ def decode_bytes(lengths, HI, DI, H, Dqk, Dv, k):
     B = len(L)
     return float((L * (DI + 4)).sum() + (np.minimum(k, L) * Dqk * 2).sum()
                  + B * (HI * DI + 4 + 4 * HI) + B * H * (Dqk + Dv) * 2 + B * k * 4)
+
+
+def decode_stage_bytes(lengths, HI, DI, H, Dqk, Dv, k):
+    """Algorithmic bytes of each decode stage's main kernel: its inputs read
+    once and its outputs written once."""
+    L = np.asarray(lengths, dtype=np.float64)
+    B = len(L)
+    K = np.minimum(k, L)
+    return {
+        # K^I cache + scales, queries + scale + weights, scores out
+        "decode_scan_kernel": float((L * (DI + 4 + 4)).sum() + B * (HI * DI + 4 + 4 * HI)),
+        # scores in (full rows), S out
+        "topk_filter_kernel": float((L * 4).sum() + B * k * 4),
+        # gathered entries, queries, S, outputs
+        "sparse_attn_kernel": float((K * Dqk * 2).sum() + B * H * Dqk * 2 + B * k * 4 + B * H * Dv * 2),
+    }
 
 
 def bench_decode(seed, steps, warmup):
@@ -154,24 +205,43 @@ def bench_decode(seed, steps, warmup):
     tws = torch.empty(tl.topk_select_workspace_bytes(B, k, max_len), dtype=torch.uint8, device=DEV)
     scale = 1.0 / math.sqrt(Dqk)
 
-    def step():
+    def f_index():
         tl.index_decode(di.q, di.k, di.w, cu, max_len, q_scale=di.q_scale, k_scale=di.k_scale, scores=scores)
+
+    def f_topk():
         tl.topk_select(scores, row_start, row_len, k, max_len, S=S, workspace=tws)
+
+    def f_attn():
         tl.sparse_attn_decode(qa, kva, cu, S, scale, Dv, out=out, workspace=ws)
 
-    wall, ev = time_calls(step, steps, warmup)
-    # per-stage event timing
-    stages = {}
-    for name, fn in (("index_decode", lambda: tl.index_decode(di.q, di.k, di.w, cu, max_len, q_scale=di.q_scale,
-                                                               k_scale=di.k_scale, scores=scores)),
-                     ("topk_select", lambda: tl.topk_select(scores, row_start, row_len, k, max_len, S=S, workspace=tws)),
-                     ("sparse_attn_decode", lambda: tl.sparse_attn_decode(qa, kva, cu, S, scale, Dv, out=out,
-                                                                          workspace=ws))):
-        stages[name] = time_calls(fn, max(3, steps // 2), 1)[1]
+    def step():
+        f_index()
+        f_topk()
+        f_attn()
+
+    tm = time_calls(step, steps, warmup)
     nbytes = decode_bytes(lengths, HI, DI, H, Dqk, Dv, k)
-    gbs = nbytes / (ev * 1e-3) / 1e9
-    log(f"decode: {ev:.3f} ms/step, {gbs:.0f} GB/s, stages {stages}")
-    planted_hit = None
+    gbs = nbytes / (tm.ev_med * 1e-3) / 1e9
+    # per stage: the whole call, and its main kernel on its own events
+    sbytes = decode_stage_bytes(lengths, HI, DI, H, Dqk, Dv, k)
+    stages = {}
+    for name, fn, kerns in (("index_decode", f_index, ("decode_scan_kernel",)),
+                            ("topk_select", f_topk, ("topk_threshold_kernel", "topk_filter_kernel",
+                                                     "topk_final_kernel")),
+                            ("sparse_attn_decode", f_attn, ("sparse_attn_kernel", "attn_combine_kernel"))):
+        st = None
+        kd = {}
+        for kern in kerns:
+            st = time_calls(fn, max(5, steps // 2), 1, kernel=kern)
+            kd[kern] = {"kernel_ms_avg": st.kernel_avg}
+            if kern in sbytes:
+                kg = sbytes[kern] / (st.kernel_avg * 1e-3) / 1e9
+                kd[kern].update(algorithmic_bytes=sbytes[kern], gbs=kg, frac=kg / PEAK_HBM_GBS)
+        stages[name] = dict(event_ms_median=st.ev_med, event_ms_min=st.ev_min, kernels=kd)
+    log(f"decode: {tm.ev_med:.3f} ms/step (median; min {tm.ev_min:.3f}), {gbs:.0f} GB/s; stages " +
+        "; ".join(f"{n_}: {v['event_ms_median']:.3f} ms (" +
+                  ", ".join(f"{kn} {kv['kernel_ms_avg']:.3f} ms" + (f" {kv['gbs']:.0f} GB/s" if 'gbs' in kv else "")
+                            for kn, kv in v["kernels"].items()) + ")" for n_, v in stages.items()))
     Sh = S.cpu().numpy()
     hit = tot = 0
     for b, pos in di.planted.items():
@@ -182,9 +252,36 @@ def bench_decode(seed, steps, warmup):
     del qa, kva, di
     return dict(workload=f"decode step: {B} sequences, L ~ U[16384,131072] (sumL={int(lengths.sum())}), "
                          f"fp8 indexer H^I={HI} d^I={DI}, top-{k}, bf16 attention H={H} Dqk={Dqk} Dv={Dv}",
-                tokens_per_s=B / (wall * 1e-3), ms_per_step=wall, kernel_ms=ev, bytes_per_step=nbytes,
-                achieved_gbs=gbs, peak_gbs=PEAK_HBM_GBS, frac=gbs / PEAK_HBM_GBS, stage_ms=stages,
-                planted_recall=planted_hit)
+                tokens_per_s=B / (tm.wall * 1e-3), bytes_per_step=nbytes, achieved_gbs=gbs,
+                peak_gbs=PEAK_HBM_GBS, frac=gbs / PEAK_HBM_GBS, stages=stages, planted_recall=planted_hit,
+                **tm.as_dict())
+
+
+def calibrate(steps):
+    """Achievable rates on this device: a streaming copy and matrix-core loops."""
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=DEV).fill_(1)
+    dst = torch.empty_like(src)
+    tm = time_calls(lambda: tl.calib_copy(src, dst), max(5, steps // 2), 2, kernel="calib_copy_kernel")
+    copy_gbs = 2.0 * nbytes / (tm.kernel_avg * 1e-3) / 1e9
+    del src, dst
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(cus * 8 * 256, dtype=torch.float32, device=DEV)
+    res = dict(copy_bytes=nbytes, copy_gbs=copy_gbs, copy_frac_of_peak=copy_gbs / PEAK_HBM_GBS)
+    for name, dt, iters, peak in (("bf16", tl.BF16, 4000, PEAK_BF16_TFLOPS), ("fp8", tl.FP8_E4M3, 2000,
+                                                                              PEAK_FP8_TFLOPS)):
+        fl = [0.0]
+
+        def run():
+            fl[0] = tl.calib_mfma(dt, cus * 8, iters, sink)
+
+        t = time_calls(run, 5, 1, kernel="calib_mfma_kernel")
+        tf = fl[0] / (t.kernel_avg * 1e-3) / 1e12
+        res[f"mfma_{name}_tflops"] = tf
+        res[f"mfma_{name}_frac_of_peak"] = tf / peak
+    log("calibration: copy {copy_gbs:.0f} GB/s, bf16 loop {mfma_bf16_tflops:.0f} TFLOP/s, "
+        "fp8 loop {mfma_fp8_tflops:.0f} TFLOP/s".format(**res))
+    return res
 
 
 def cpu_baseline(inp, k, n, target_s=15.0):
@@ -214,6 +311,35 @@ def cpu_baseline(inp, k, n, target_s=15.0):
                        f"({pairs} causal pairs, {dt:.1f} s, double precision, OpenMP over rows)")
 
 
+# HBM traffic of the headline kernel per launch, from two rocprofv3 --pmc runs of
+# `bench.py --quick --no-cpu --steps 3 --warmup 1` (FETCH_SIZE, then WRITE_SIZE,
+# KiB per dispatch, averaged over the dispatches of the kernel), each scaled by
+# the same counter's reading for the 1 GiB calibration copy in the same run.
+# The figures hold only for the kernel sources they were taken on: when the
+# hash of those sources differs, the traffic is reported as null.
+TRAFFIC_SOURCES = ("indexer.hip", "tlsl_device.h", "tlsl_internal.h", "topk_common.h")
+TRAFFIC = {
+    "prefill_score_kernel": None,
+}
+
+
+def sources_sha256(names):
+    import hashlib
+    h = hashlib.sha256()
+    for nm in names:
+        with open(os.path.join(ROOT, "token_level_sparse_lightning_amd", "csrc", nm), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel):
+    rec = TRAFFIC.get(kernel)
+    if not rec or rec["sources_sha256"] != sources_sha256(TRAFFIC_SOURCES):
+        return None
+    copy = float(rec["copy_bytes"])
+    return (rec["fetch_kib"] * copy / rec["copy_fetch_kib"] + rec["write_kib"] * copy / rec["copy_write_kib"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,10 +347,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--long", action="store_true", help="also time the n=131072 prefill")
-    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--quick", action="store_true", help="headline workload (and calibration) only")
     ap.add_argument("--only", default="", help="comma list of extra workloads to run: "
                     "prefill_fp8,attn_prefill,decode,prefill_long (default: all but prefill_long)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-calib", action="store_true", help="skip the copy and matrix-core calibration")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (every workload runs on one "
@@ -252,8 +379,17 @@ def main():
         if "prefill_long" in want:
             lg, _, _ = bench_prefill(131072, synth.DT_FP8, args.seed + 4, 3, 1, plant_max_dist=100000)
             extra["prefill_long"] = lg
+    calib = None if args.no_calib else calibrate(args.steps)
     cpu = None if args.no_cpu else cpu_baseline(inp, 2048, 8192)
 
+    roofline = {"bound": "mfma", "achieved": head["kernel_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": head["frac"], "traffic": recorded_traffic("prefill_score_kernel"),
+                "kernel": "prefill_score_kernel", "kernel_ms": head["kernel_ms_avg"],
+                "launches": head["kernel_launches"], "flops_per_launch": head["flops_per_call"],
+                "algorithmic_bytes_per_launch": head["algorithmic_bytes_per_call"]}
+    if calib:
+        roofline["measured_peak"] = calib["mfma_bf16_tflops"]
+        roofline["frac_of_measured_peak"] = head["kernel_tflops"] / calib["mfma_bf16_tflops"]
     line = {
         "metric": "indexer+top-k query-key pairs/s (prefill)",
         "value": head["pairs_per_s"],
@@ -269,12 +405,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": head["workload"], "B": 1, "n": 8192, "H_I": 64, "d_I": 128, "k": 2048,
                    "seed": args.seed},
-        "roofline": {"bound": "mfma", "achieved": head["achieved_tflops"], "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": head["frac"], "traffic": None,
-                     "kernel": "index_prefill (score + finalize + fallback kernels)",
-                     "flops_per_launch": head["flops_per_call"], "kernel_ms": head["kernel_ms"]},
+        "roofline": roofline,
         "cpu_baseline": cpu,
-        "planted_recall": head["planted_recall"],
+        "headline": head,
+        "calibration": calib,
         "extra": extra,
     }
     print(json.dumps(line), flush=True)

@@ -13,6 +13,8 @@ from token_level_sparse_lightning_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tlsl.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6
 
@@ -24,13 +26,16 @@ def _lib():
     return tl.load()
 
 
-def _declared():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+def _declared(headers=None):
+    names = set()
+    for h in headers or HEADERS:
+        text = open(h).read()
+        names |= set(re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_five_calls():
-    names = _declared()
+    names = _declared([HEADER])
     for fn in ("index_prefill", "index_decode", "topk_select", "sparse_attn_prefill",
                "sparse_attn_decode", "tlsl_last_error", "tlsl_version"):
         assert fn in names
@@ -38,9 +43,28 @@ def test_header_declares_the_five_calls():
 
 def test_every_declared_symbol_is_exported():
     lib = _lib()
-    for fn in _declared():
+    names = _declared()
+    assert "tlsl_timer_arm" in names and "tlsl_calib_copy" in names
+    for fn in names:
         assert hasattr(lib, fn), fn
+    assert set(binding.EXPORTS) == set(names)
     assert lib.tlsl_version().startswith(b"tlsl")
+
+
+def test_measurement_validation():
+    """Host-side checks of the measurement aids (no event or launch is made)."""
+    lib = _lib()
+    assert lib.tlsl_timer_arm(None, 4) == ERR_NULL
+    assert lib.tlsl_timer_arm(b"prefill_score_kernel", 0) == ERR_SHAPE
+    assert lib.tlsl_timer_arm(b"prefill_score_kernel", 70000) == ERR_SHAPE
+    assert lib.tlsl_timer_collect(None, None, None, None) == ERR_SHAPE      # not armed
+    assert lib.tlsl_calib_copy(None, P, 16, None) == ERR_NULL
+    assert lib.tlsl_calib_copy(P, P, 17, None) == ERR_SHAPE
+    assert lib.tlsl_calib_copy(MIS, P, 16, None) == ERR_ALIGN
+    d = ctypes.c_double(0)
+    assert lib.tlsl_calib_mfma(1, 0, 4, P, ctypes.byref(d), None) == ERR_SHAPE
+    assert lib.tlsl_calib_mfma(0, 4, 4, P, ctypes.byref(d), None) == ERR_UNSUP
+    assert b"bf16" in lib.tlsl_last_error()
 
 
 P = ctypes.c_void_p(256)      # aligned dummy device pointer: never dereferenced here

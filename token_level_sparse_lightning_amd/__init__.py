@@ -8,6 +8,8 @@ from .binding import (  # noqa: F401
     F32,
     FP8_E4M3,
     TlslError,
+    calib_copy,
+    calib_mfma,
     index_decode,
     index_prefill,
     index_prefill_workspace_bytes,
@@ -15,6 +17,8 @@ from .binding import (  # noqa: F401
     sparse_attn_decode,
     sparse_attn_decode_workspace_bytes,
     sparse_attn_prefill,
+    timer_arm,
+    timer_collect,
     topk_select,
     topk_select_workspace_bytes,
 )

@@ -18,7 +18,9 @@ LIB_PATH = os.path.join(_PKG, "libtlsl.so")
 F32, BF16, FP8_E4M3 = 0, 1, 2
 
 EXPORTS = ("index_prefill", "index_decode", "topk_select", "sparse_attn_prefill",
-           "sparse_attn_decode", "tlsl_last_error", "tlsl_version")
+           "sparse_attn_decode", "tlsl_last_error", "tlsl_version",
+           # measurement aids (include/tlsl_measure.h)
+           "tlsl_timer_arm", "tlsl_timer_collect", "tlsl_calib_copy", "tlsl_calib_mfma")
 
 _lib = None
 
@@ -49,6 +51,13 @@ def load():
         getattr(lib, fn).restype = I
     lib.tlsl_last_error.restype = ctypes.c_char_p
     lib.tlsl_version.restype = ctypes.c_char_p
+    D = ctypes.POINTER(ctypes.c_double)
+    lib.tlsl_timer_arm.argtypes = [ctypes.c_char_p, I]
+    lib.tlsl_timer_collect.argtypes = [ctypes.POINTER(I), D, D, D]
+    lib.tlsl_calib_copy.argtypes = [P, P, ctypes.c_size_t, P]
+    lib.tlsl_calib_mfma.argtypes = [I, I, I, P, D, P]
+    for fn in ("tlsl_timer_arm", "tlsl_timer_collect", "tlsl_calib_copy", "tlsl_calib_mfma"):
+        getattr(lib, fn).restype = I
     _lib = lib
     return lib
 
@@ -210,3 +219,40 @@ def sparse_attn_decode(q, kv_cache, cu_seqlens, S, softmax_scale, Dv, out=None, 
                                 _ptr(workspace), ctypes.byref(size), _stream(stream))
     _check("sparse_attn_decode", rc)
     return out, lse
+
+
+# ---- measurement aids (include/tlsl_measure.h) --------------------------------
+def timer_arm(kernel: str, max_launches: int = 4096) -> None:
+    """Bracket every following launch of ``kernel`` with HIP events on its stream."""
+    lib = load()
+    _check("tlsl_timer_arm", lib.tlsl_timer_arm(kernel.encode(), int(max_launches)))
+
+
+def timer_collect():
+    """Disarm the kernel timer: (launches, total_ms, min_ms, max_ms)."""
+    lib = load()
+    n = ctypes.c_int(0)
+    tot, mn, mx = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_double(0)
+    _check("tlsl_timer_collect", lib.tlsl_timer_collect(ctypes.byref(n), ctypes.byref(tot), ctypes.byref(mn),
+                                                        ctypes.byref(mx)))
+    return n.value, tot.value, mn.value, mx.value
+
+
+def calib_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Streaming copy of src's bytes into dst (the HBM-bandwidth calibration kernel)."""
+    lib = load()
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    _check("tlsl_calib_copy", lib.tlsl_calib_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+def calib_mfma(dt: int, blocks: int, iters: int, sink: torch.Tensor, stream=None) -> float:
+    """Matrix-core loop (the MFMA-rate calibration kernel); returns its flop count."""
+    lib = load()
+    if sink.dtype != torch.float32 or sink.numel() < blocks * 256:
+        raise ValueError("sink must hold blocks*256 float32")
+    fl = ctypes.c_double(0)
+    _check("tlsl_calib_mfma", lib.tlsl_calib_mfma(int(dt), int(blocks), int(iters), _ptr(sink), ctypes.byref(fl),
+                                                  _stream(stream)))
+    return fl.value

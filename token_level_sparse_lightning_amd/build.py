@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtlsl.so")
 
-SOURCES = ["abi.cpp", "indexer.hip", "topk.hip", "attn.hip"]
+SOURCES = ["abi.cpp", "indexer.hip", "topk.hip", "attn.hip", "measure.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -31,6 +31,11 @@ HIPCC_FLAGS = [
 ]
 
 
+# per-source flags: the calibration loop keeps its loop-carried accumulators in
+# VGPRs (the AGPR form makes the compiler rotate them through copies)
+SOURCE_FLAGS = {"measure.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _hipcc() -> str:
     for cand in ("/opt/rocm/bin/hipcc", "hipcc"):
         if os.path.isabs(cand) and os.path.exists(cand):
@@ -40,7 +45,7 @@ def _hipcc() -> str:
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -73,6 +73,18 @@ int check_indexer(int dt, const void* q, const float* q_scale, const void* k, co
 
 }  // namespace
 
+int tlsl::report(int code, const char* fmt, ...) {
+    if (code == TLSL_OK || !fmt) {
+        g_err[0] = '\0';
+        return code;
+    }
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
 extern "C" {
 
 const char* tlsl_last_error(void) { return g_err; }

@@ -30,11 +30,15 @@ namespace tlsl {
 constexpr int AT_TS = 32;      // slots per tile
 constexpr int AT_KMAX = 4096;  // slots per workgroup (k <= 4096)
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats to packed bf16 (round to nearest even; one gfx950 instruction)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return (uint16_t)pack_bf16x2(f, 0.f); }
 
 struct AttnArgs {
     const unsigned char* q;   // [rows][H][Dqk]
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     // group reads for the logits fall in distinct banks
     __shared__ __align__(16) unsigned char ctile[AT_TS * CSTR + (AT_TS / 16) * 64];
     __shared__ __align__(16) unsigned char vt[DV * VSTR];
-    __shared__ int slots[AT_KMAX];            // the row's slot range: position or -1
+    __shared__ __align__(16) int slots[AT_KMAX];  // the row's slot range: position or -1
     __shared__ int tile_any[AT_KMAX / AT_TS];
     __shared__ int tlist[AT_KMAX / AT_TS];
     __shared__ int ntl_sh;
@@ -165,33 +169,44 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
         uint4 v[VPER][4];
         uint4 r[RPER > 0 ? RPER : 1];
     };
+    // each thread gathers the same (slot quad, chunk) items of every tile:
+    // their base addresses are fixed, a load adds the slot's entry offset
+    const unsigned char* kvrow = a.kv + (size_t)kv_base * CROW;
+    int vqd[VPER], rrow[RPER > 0 ? RPER : 1];
+    const unsigned char* vsrc[VPER];
+    const unsigned char* rsrc[RPER > 0 ? RPER : 1];
+#pragma unroll
+    for (int j = 0; j < VPER; ++j) {
+        // items past the end repeat the last one, so every thread issues the
+        // same loads and the compiler's wait counts stay exact
+        const int it = min(tid + j * NT, VITEMS - 1);
+        vqd[j] = it % (AT_TS / 4);  // slot quad varies fastest across lanes
+        vsrc[j] = kvrow + (it / (AT_TS / 4)) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < RPER; ++j) {
+        const int it = min(tid + j * NT, RITEMS - 1);
+        rrow[j] = it / RC;
+        rsrc[j] = kvrow + (DV / VPC + it % RC) * 16;
+    }
     auto load_tile = [&](int t, Pre& P) {
         const int* sl = slots + t * AT_TS;
-        // every thread issues the same loads (items past the end repeat the
-        // last one) so that the compiler's wait counts stay exact
 #pragma unroll
         for (int j = 0; j < VPER; ++j) {
-            const int it = min(tid + j * NT, VITEMS - 1);
-            {
-                // slot quad varies fastest across lanes (spreads the transposed writes)
-                const int qd = it % (AT_TS / 4), oc = it / (AT_TS / 4);
+            const int4 q4 = *reinterpret_cast<const int4*>(sl + 4 * vqd[j]);
+            const int qs[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    // an invalid slot reads the row's entry 0 (always in bounds):
-                    // its logit is masked to -inf, so its probability is exactly 0
-                    const int pos = max(sl[4 * qd + u], 0);
-                    P.v[j][u] = *reinterpret_cast<const uint4*>(a.kv + (size_t)(kv_base + pos) * CROW + oc * 16);
-                }
+            for (int u = 0; u < 4; ++u) {
+                // an invalid slot reads the row's entry 0 (always in bounds):
+                // its logit is masked to -inf, so its probability is exactly 0
+                const uint32_t pos = (uint32_t)max(qs[u], 0);
+                P.v[j][u] = *reinterpret_cast<const uint4*>(vsrc[j] + (size_t)pos * CROW);
             }
         }
 #pragma unroll
         for (int j = 0; j < RPER; ++j) {
-            const int it = min(tid + j * NT, RITEMS - 1);
-            {
-                const int r = it / RC, oc = DV / VPC + it % RC;
-                const int pos = max(sl[r], 0);
-                P.r[j] = *reinterpret_cast<const uint4*>(a.kv + (size_t)(kv_base + pos) * CROW + oc * 16);
-            }
+            const uint32_t pos = (uint32_t)max(sl[rrow[j]], 0);
+            P.r[j] = *reinterpret_cast<const uint4*>(rsrc[j] + (size_t)pos * CROW);
         }
     };
     auto store_tile = [&](const Pre& P) {
@@ -255,11 +270,19 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
         {
             const uint4* cp0 = reinterpret_cast<const uint4*>(ctile + crow(8 * (c >> 2) + (c & 3)) + (kd0 + g * (QKD / 4)) * EB);
             const uint4* cp1 = reinterpret_cast<const uint4*>(ctile + crow(8 * (c >> 2) + 4 + (c & 3)) + (kd0 + g * (QKD / 4)) * EB);
+            uint4 ca[NCQ], cb[NCQ];
+#pragma unroll
+            for (int ch = 0; ch < NCQ; ++ch) {
+                ca[ch] = cp0[ch];
+                cb[ch] = cp1[ch];
+            }
+            // every fragment read is in flight before the first product
+            __builtin_amdgcn_sched_barrier(0);
             v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ch = 0; ch < NCQ; ++ch) {
-                acc0 = mma_chunk(cp0[ch], qf[ch], acc0);
-                acc1 = mma_chunk(cp1[ch], qf[ch], acc1);
+                acc0 = mma_chunk(ca[ch], qf[ch], acc0);
+                acc1 = mma_chunk(cb[ch], qf[ch], acc1);
             }
             if constexpr (DSPLIT > 1) {
                 // add the partner wave's partial logits (the same sum in both waves)
@@ -276,40 +299,47 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
                 z[4 + r] = sl[8 * g + 4 + r] >= 0 ? acc1[r] * a.scale_log2 : -INFINITY;
             }
         }
+        // V^T fragments of the tile, read before the softmax so that their
+        // latency overlaps it
+        uint4 vb[NDB][NCP];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const uint4* vp = reinterpret_cast<const uint4*>(vt + (half * DVW + 16 * db + c) * VSTR + g * (VROW / 4));
+#pragma unroll
+            for (int ch = 0; ch < NCP; ++ch) vb[db][ch] = vp[ch];
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // ---- online softmax per head -----------------------------------------
         float mx = z[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mx = fmaxf(mx, z[j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        float p[8];
-        float alpha = 1.f;
-        if (m_new == -INFINITY) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) p[j] = 0.f;
-        } else {
-            alpha = exp2f(m_run - m_new);
-            float ps = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                p[j] = exp2f(z[j] - m_new);
-                ps += p[j];
-            }
-            l_run = l_run * alpha + ps;
-            m_run = m_new;
-        }
-        if (__ballot(alpha != 1.f)) {
+        mx = xor32_max(xor16_max(mx));
+        // lazy reference: it moves only when a logit exceeds it by more than 8
+        // (a factor 256), so the weights stay <= 256 and rescaling the
+        // accumulators is rare; the normalised result does not depend on it
+        const bool grow = mx > m_run + 8.f;  // any finite mx while m_run = -inf
+        if (__ballot(grow)) {
+            const float m_new = grow ? mx : m_run;
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 from -inf
 #pragma unroll
             for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+            l_run *= alpha;
+            m_run = m_new;
         }
+        const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+        float p[8];
+        float ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[j] = __builtin_amdgcn_exp2f(z[j] - m_ref);  // z - m_ref <= 8; -inf gives 0
+            ps += p[j];
+        }
+        l_run += ps;
         // P^T fragment: column = head c, slots 8g..8g+7
         uint4 pf[NCP];
         if constexpr (EB == 2) {
-            pf[0] = make_uint4((uint32_t)f32_to_bf16_rne(p[0]) | ((uint32_t)f32_to_bf16_rne(p[1]) << 16),
-                               (uint32_t)f32_to_bf16_rne(p[2]) | ((uint32_t)f32_to_bf16_rne(p[3]) << 16),
-                               (uint32_t)f32_to_bf16_rne(p[4]) | ((uint32_t)f32_to_bf16_rne(p[5]) << 16),
-                               (uint32_t)f32_to_bf16_rne(p[6]) | ((uint32_t)f32_to_bf16_rne(p[7]) << 16));
+            pf[0] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                               pack_bf16x2(p[6], p[7]));
         } else {
             pf[0] = make_uint4(__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]), __float_as_uint(p[3]));
             pf[1] = make_uint4(__float_as_uint(p[4]), __float_as_uint(p[5]), __float_as_uint(p[6]), __float_as_uint(p[7]));
@@ -317,9 +347,8 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
         // ---- O^T[d][head] += V^T[d][slots] P^T[slots][head] -------------------
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            const uint4* vp = reinterpret_cast<const uint4*>(vt + (half * DVW + 16 * db + c) * VSTR + g * (VROW / 4));
 #pragma unroll
-            for (int ch = 0; ch < NCP; ++ch) o[db] = mma_chunk(vp[ch], pf[ch], o[db]);
+            for (int ch = 0; ch < NCP; ++ch) o[db] = mma_chunk(vb[db][ch], pf[ch], o[db]);
         }
     };
     Pre P;
@@ -339,8 +368,7 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     }
 
     // ---- finish --------------------------------------------------------------
-    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float l_tot = xor32_sum(xor16_sum(l_run));
     if (!hvalid) return;
     if (a.part_o) {
         // split: unnormalised partials of this wave's value dims
@@ -361,8 +389,7 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     for (int db = 0; db < NDB; ++db) {
         const int d0 = 16 * db + 4 * g;
         if constexpr (EB == 2) {
-            uint2 pk = make_uint2((uint32_t)f32_to_bf16_rne(o[db][0] * inv) | ((uint32_t)f32_to_bf16_rne(o[db][1] * inv) << 16),
-                                  (uint32_t)f32_to_bf16_rne(o[db][2] * inv) | ((uint32_t)f32_to_bf16_rne(o[db][3] * inv) << 16));
+            uint2 pk = make_uint2(pack_bf16x2(o[db][0] * inv, o[db][1] * inv), pack_bf16x2(o[db][2] * inv, o[db][3] * inv));
             *reinterpret_cast<uint2*>(op + d0 * 2) = pk;
         } else {
             *reinterpret_cast<float4*>(op + d0 * 4) = make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
@@ -447,8 +474,9 @@ static void launch_attn_t(AttnArgs a, int rows, hipStream_t st) {
     const int hg = (a.H + HPW - 1) / HPW;
     a.rows = rows;
     const int grid = hg == 1 ? rows : (rows + 7) / 8 * 8 * hg;
-    hipLaunchKernelGGL((sparse_attn_kernel<DT, HBW, DSPLIT, DQK, DV, DEC>), dim3(grid), dim3(HBW * DSPLIT * 64), 0, st,
-                       a);
+    TLSL_TIMED_LAUNCH("sparse_attn_kernel", st,
+                      hipLaunchKernelGGL((sparse_attn_kernel<DT, HBW, DSPLIT, DQK, DV, DEC>), dim3(grid),
+                                         dim3(HBW * DSPLIT * 64), 0, st, a));
 }
 
 template <bool DEC>
@@ -501,11 +529,13 @@ hipError_t launch_sparse_attn_decode(const AttnShape& s, const void* q, const vo
     dispatch_attn<true>(s, a, B * ns, st);
     if (ns > 1) {
         if (s.dt == kBF16)
-            hipLaunchKernelGGL((attn_combine_kernel<kBF16, 512>), dim3(B * s.H), dim3(CB_NT), 0, st, a.part_o, a.part_ml,
-                               s.H, ns, a.out, lse);
+            TLSL_TIMED_LAUNCH("attn_combine_kernel", st,
+                              hipLaunchKernelGGL((attn_combine_kernel<kBF16, 512>), dim3(B * s.H), dim3(CB_NT), 0, st,
+                                                 a.part_o, a.part_ml, s.H, ns, a.out, lse));
         else
-            hipLaunchKernelGGL((attn_combine_kernel<kF32, 64>), dim3(B * s.H), dim3(CB_NT), 0, st, a.part_o, a.part_ml,
-                               s.H, ns, a.out, lse);
+            TLSL_TIMED_LAUNCH("attn_combine_kernel", st,
+                              hipLaunchKernelGGL((attn_combine_kernel<kF32, 64>), dim3(B * s.H), dim3(CB_NT), 0, st,
+                                                 a.part_o, a.part_ml, s.H, ns, a.out, lse));
     }
     return hipGetLastError();
 }

@@ -706,16 +706,24 @@ template <int DT, int HB, int DI>
 static hipError_t launch_prefill_t(const PrefillArgs& pa, const FinalizeArgs& fa, const FallbackArgs& fb,
                                    int qw, int rows, int cap, int fb_blocks, hipStream_t st) {
     if (qw == 2)
-        hipLaunchKernelGGL((prefill_score_kernel<DT, HB, DI, 2>), dim3(pa.tiles * pa.B), dim3(PF_NT), 0, st, pa);
+        TLSL_TIMED_LAUNCH("prefill_score_kernel", st,
+                          hipLaunchKernelGGL((prefill_score_kernel<DT, HB, DI, 2>), dim3(pa.tiles * pa.B), dim3(PF_NT), 0,
+                                             st, pa));
     else
-        hipLaunchKernelGGL((prefill_score_kernel<DT, HB, DI, 1>), dim3(pa.tiles * pa.B), dim3(PF_NT), 0, st, pa);
+        TLSL_TIMED_LAUNCH("prefill_score_kernel", st,
+                          hipLaunchKernelGGL((prefill_score_kernel<DT, HB, DI, 1>), dim3(pa.tiles * pa.B), dim3(PF_NT), 0,
+                                             st, pa));
     if (cap <= 1024)
-        hipLaunchKernelGGL((prefill_finalize_kernel<1024>), dim3(rows), dim3(FIN_NT), 0, st, fa);
+        TLSL_TIMED_LAUNCH("prefill_finalize_kernel", st,
+                          hipLaunchKernelGGL((prefill_finalize_kernel<1024>), dim3(rows), dim3(FIN_NT), 0, st, fa));
     else if (cap <= 4352)
-        hipLaunchKernelGGL((prefill_finalize_kernel<4352>), dim3(rows), dim3(FIN_NT), 0, st, fa);
+        TLSL_TIMED_LAUNCH("prefill_finalize_kernel", st,
+                          hipLaunchKernelGGL((prefill_finalize_kernel<4352>), dim3(rows), dim3(FIN_NT), 0, st, fa));
     else
-        hipLaunchKernelGGL((prefill_finalize_kernel<8448>), dim3(rows), dim3(FIN_NT), 0, st, fa);
-    hipLaunchKernelGGL((prefill_fallback_kernel<DT, HB, DI>), dim3(fb_blocks), dim3(FB_NT), 0, st, fb);
+        TLSL_TIMED_LAUNCH("prefill_finalize_kernel", st,
+                          hipLaunchKernelGGL((prefill_finalize_kernel<8448>), dim3(rows), dim3(FIN_NT), 0, st, fa));
+    TLSL_TIMED_LAUNCH("prefill_fallback_kernel", st,
+                      hipLaunchKernelGGL((prefill_fallback_kernel<DT, HB, DI>), dim3(fb_blocks), dim3(FB_NT), 0, st, fb));
     return hipGetLastError();
 }
 
@@ -801,15 +809,17 @@ static hipError_t launch_decode_t(const void* q, const float* q_scale, const voi
             per_cu = nb;
         }
         const int grid = std::min(device_cu_count() * per_cu, std::max(1, (int)(((int64_t)max_len * B + 63) / 64)));
-        hipLaunchKernelGGL((decode_scan_kernel<DT, HB, DI>), dim3(grid), dim3(DEC2_NT), 0, st,
-                           static_cast<const unsigned char*>(q), q_scale, static_cast<const unsigned char*>(kc),
-                           k_scale, w, cu, B, HI, scores);
+        TLSL_TIMED_LAUNCH("decode_scan_kernel", st,
+                          hipLaunchKernelGGL((decode_scan_kernel<DT, HB, DI>), dim3(grid), dim3(DEC2_NT), 0, st,
+                                             static_cast<const unsigned char*>(q), q_scale,
+                                             static_cast<const unsigned char*>(kc), k_scale, w, cu, B, HI, scores));
         return hipGetLastError();
     }
     dim3 grid((max_len + DEC_CHUNK - 1) / DEC_CHUNK, B);
-    hipLaunchKernelGGL((decode_score_kernel<DT, HB, DI>), grid, dim3(DEC_NT), 0, st,
-                       static_cast<const unsigned char*>(q), q_scale, static_cast<const unsigned char*>(kc),
-                       k_scale, w, cu, HI, scores);
+    TLSL_TIMED_LAUNCH("decode_score_kernel", st,
+                      hipLaunchKernelGGL((decode_score_kernel<DT, HB, DI>), grid, dim3(DEC_NT), 0, st,
+                                         static_cast<const unsigned char*>(q), q_scale,
+                                         static_cast<const unsigned char*>(kc), k_scale, w, cu, HI, scores));
     return hipGetLastError();
 }
 

@@ -105,6 +105,29 @@ __device__ __forceinline__ float reduce_heads_64(const float part[4]) {
 }
 
 // ---------------------------------------------------------------------------
+// Butterfly steps across 16-lane rows (lane l with l^16) and across wave
+// halves (l with l^32) through the permlane swaps: no LDS traffic, so they do
+// not wait behind outstanding LDS reads.  Both lanes of a pair get the same
+// bits (max and + are commutative).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float xor16_max(float x) {
+    auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// ---------------------------------------------------------------------------
 // Order-preserving 32-bit key of an fp32 score: larger score <=> larger key,
 // -0.0 and +0.0 map to the same key.
 // ---------------------------------------------------------------------------

@@ -11,6 +11,21 @@ namespace tlsl {
 // Compute units of the current device (queried once per device).
 int device_cu_count();
 
+// Sets the thread-local message that tlsl_last_error returns (cleared for
+// TLSL_OK) and returns `code`.
+int report(int code, const char* fmt, ...);
+
+// Kernel timer hook: records the armed event pair around a launch of the
+// kernel called `kernel` on stream `st` (no-op unless that kernel is armed).
+void timer_mark(const char* kernel, hipStream_t st, bool after);
+
+#define TLSL_TIMED_LAUNCH(name, st, ...)        \
+    do {                                        \
+        ::tlsl::timer_mark(name, st, false);    \
+        __VA_ARGS__;                            \
+        ::tlsl::timer_mark(name, st, true);     \
+    } while (0)
+
 // ---- indexer ---------------------------------------------------------------
 struct IndexerShape {
     int dt;      // 0 f32, 1 bf16, 2 fp8

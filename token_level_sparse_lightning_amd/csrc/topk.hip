@@ -269,10 +269,11 @@ hipError_t launch_topk_select(const float* scores, const int64_t* row_start, con
     a.buf = reinterpret_cast<uint2*>(w + a256((size_t)R * sizeof(float)) + a256((size_t)R * TSEL_CNT_STRIDE * sizeof(int)));
     a.S = S;
     a.Ss = S_score;
-    hipLaunchKernelGGL(topk_threshold_kernel, dim3(R), dim3(TT_NT), 0, st, a);
+    TLSL_TIMED_LAUNCH("topk_threshold_kernel", st, hipLaunchKernelGGL(topk_threshold_kernel, dim3(R), dim3(TT_NT), 0, st, a));
     const int chunks = max_len > 0 ? (max_len + TF_CHUNK - 1) / TF_CHUNK : 1;
-    hipLaunchKernelGGL(topk_filter_kernel, dim3(chunks, R), dim3(TF_NT), 0, st, a);
-    hipLaunchKernelGGL(topk_final_kernel, dim3(R), dim3(TFIN_NT), 0, st, a);
+    TLSL_TIMED_LAUNCH("topk_filter_kernel", st,
+                      hipLaunchKernelGGL(topk_filter_kernel, dim3(chunks, R), dim3(TF_NT), 0, st, a));
+    TLSL_TIMED_LAUNCH("topk_final_kernel", st, hipLaunchKernelGGL(topk_final_kernel, dim3(R), dim3(TFIN_NT), 0, st, a));
     return hipGetLastError();
 }
 
