@@ -366,12 +366,17 @@ struct FinalizeArgs {
     int* fb_list;
 };
 
+constexpr int FIN_BLMAX = 256;  // boundary-bin keys ranked directly
+
 template <int CAPMAX>
 __global__ __launch_bounds__(FIN_NT) void prefill_finalize_kernel(FinalizeArgs a) {
-    __shared__ float fsc[CAPMAX];
+    __shared__ uint32_t fkey[CAPMAX];  // order-preserving keys, ascending position
     __shared__ int fpos[CAPMAX];
     __shared__ uint32_t hist[2048];
+    __shared__ uint32_t blist[FIN_BLMAX];
     __shared__ int scratch[64];
+    __shared__ int bcnt, gsh;
+    __shared__ uint32_t tsh;
     const int tid = threadIdx.x;
     const int row = blockIdx.x;
     const int t = row % a.n;
@@ -382,58 +387,112 @@ __global__ __launch_bounds__(FIN_NT) void prefill_finalize_kernel(FinalizeArgs a
         return;
     }
     const uint2* src = a.buf + (size_t)row * a.cap;
-    for (int i = tid; i < cnt; i += FIN_NT) {
-        const uint2 e = src[i];
-        fsc[cnt - 1 - i] = __uint_as_float(e.x);  // ascending position order
-        fpos[cnt - 1 - i] = (int)e.y;
-    }
+    if (cnt > 0)
+        batched_copy<FIN_NT, 16>(cnt, [&](int i) { return src[i]; }, [&](int i, uint2 e) {
+            fkey[cnt - 1 - i] = score_key(__uint_as_float(e.x));  // the buffer holds descending positions
+            fpos[cnt - 1 - i] = (int)e.y;
+        });
     __syncthreads();
-    uint32_t T = 0u;
-    int gt = cnt;
+    uint32_t T = 0u;  // key of the K-th largest candidate
+    int gt = cnt;     // candidates with a key above T
     if (cnt > K) {
-        uint32_t prefix = 0, pmask = 0;
-        int need = K;
-        gt = 0;
-        for (int p = 0; p < 3; ++p) {
-            const int sh = radix_shift(p);
-            const uint32_t dm = radix_mask(p);
-            for (int i = tid; i < 2048; i += FIN_NT) hist[i] = 0;
-            __syncthreads();
+        // one histogram pass over the row's own key span: 2048 bins of 2^s keys
+        uint32_t lo = 0xffffffffu, hi = 0u;
+        for (int i = tid; i < cnt; i += FIN_NT) {
+            lo = min(lo, fkey[i]);
+            hi = max(hi, fkey[i]);
+        }
+        block_minmax_u32<FIN_NT>(&lo, &hi, scratch);
+        const uint32_t span = hi - lo;
+        const int s = span < 2048u ? 0 : (32 - __clz(span)) - 11;
+        for (int i = tid; i < 2048; i += FIN_NT) hist[i] = 0;
+        if (tid == 0) bcnt = 0;
+        __syncthreads();
+        for (int i = tid; i < cnt; i += FIN_NT) atomicAdd(&hist[(fkey[i] - lo) >> s], 1u);
+        __syncthreads();
+        int above;
+        const int d = block_find_bin<FIN_NT, 2048>(hist, K, &above, scratch);
+        const int need = K - above;  // rank of the K-th largest inside bin d
+        const int nb = (int)hist[d];
+        if (s == 0) {
+            T = lo + (uint32_t)d;
+            gt = above;
+        } else if (nb <= FIN_BLMAX) {
             for (int i = tid; i < cnt; i += FIN_NT) {
-                const uint32_t key = score_key(fsc[i]);
-                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
+                const uint32_t k = fkey[i];
+                if (((k - lo) >> s) == (uint32_t)d) blist[atomicAdd(&bcnt, 1)] = k;
             }
             __syncthreads();
-            int above;
-            const int d = block_find_bin<FIN_NT, 2048>(hist, need, &above, scratch);
-            gt += above;
-            need -= above;
-            prefix |= (uint32_t)d << sh;
-            pmask |= dm << sh;
+            // rank the few boundary keys against each other
+            if (tid < nb) {
+                const uint32_t kj = blist[tid];
+                int g = 0, e = 0;
+                for (int m = 0; m < nb; ++m) {
+                    const uint32_t km = blist[m];
+                    g += km > kj;
+                    e += km == kj;
+                }
+                if (g < need && need <= g + e) {  // equal keys write equal values
+                    tsh = kj;
+                    gsh = above + g;
+                }
+            }
+            __syncthreads();
+            T = tsh;
+            gt = gsh;
+        } else {
+            // many candidates in one bin: exact 11/11/10-bit radix over all keys
+            uint32_t prefix = 0, pmask = 0;
+            int left = K;
+            gt = 0;
+            for (int p = 0; p < 3; ++p) {
+                const int sh = radix_shift(p);
+                const uint32_t dm = radix_mask(p);
+                __syncthreads();
+                for (int i = tid; i < 2048; i += FIN_NT) hist[i] = 0;
+                __syncthreads();
+                for (int i = tid; i < cnt; i += FIN_NT) {
+                    const uint32_t key = fkey[i];
+                    if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
+                }
+                __syncthreads();
+                int ab;
+                const int dd = block_find_bin<FIN_NT, 2048>(hist, left, &ab, scratch);
+                gt += ab;
+                left -= ab;
+                prefix |= (uint32_t)dd << sh;
+                pmask |= dm << sh;
+            }
+            T = prefix;
         }
-        T = prefix;
     }
     const int need_ties = K - gt;
     int32_t* Srow = a.S + (size_t)row * a.topk;
     float* Ssrow = a.Ss ? a.Ss + (size_t)row * a.topk : nullptr;
-    int run_sel = 0, run_tie = 0;
-    for (int base = 0; base < cnt && run_sel < K; base += FIN_NT) {
-        const int i = base + tid;
-        const bool v = i < cnt;
-        const float s = v ? fsc[i] : 0.f;
-        const uint32_t key = v ? score_key(s) : 0u;
-        const bool isgt = v && key > T, istie = v && key == T;
-        int rt, rdum, tt, tdum;
-        block_scan2<FIN_NT>(istie, false, &rt, &rdum, &tt, &tdum, scratch);
-        const bool sel = isgt || (istie && run_tie + rt < need_ties);
-        int rs, ts;
-        block_scan2<FIN_NT>(sel, false, &rs, &rdum, &ts, &tdum, scratch);
+    // ordered output: each thread owns a contiguous run of the (ascending)
+    // candidates; one scan gives the slot of its first selected entry.  Ties
+    // with the K-th key are taken in position order until K are selected.
+    const int seg = (cnt + FIN_NT - 1) / FIN_NT;
+    const int b0 = min(tid * seg, cnt), b1 = min(b0 + seg, cnt);
+    int ngt = 0, ntie = 0;
+    for (int i = b0; i < b1; ++i) {
+        const uint32_t key = fkey[i];
+        ngt += key > T;
+        ntie += key == T;
+    }
+    int egt, etie, tgt, ttie;
+    block_scan_int2<FIN_NT>(ngt, ntie, &egt, &etie, &tgt, &ttie, scratch);
+    int slot = egt + min(etie, need_ties);
+    int ties_before = etie;
+    for (int i = b0; i < b1; ++i) {
+        const uint32_t key = fkey[i];
+        bool sel = key > T;
+        if (key == T) sel = ties_before++ < need_ties;
         if (sel) {
-            Srow[run_sel + rs] = fpos[i];
-            if (Ssrow) Ssrow[run_sel + rs] = s;
+            Srow[slot] = fpos[i];
+            if (Ssrow) Ssrow[slot] = key_score(key);
+            ++slot;
         }
-        run_sel += ts;
-        run_tie += tt;
     }
     for (int i = K + tid; i < a.topk; i += FIN_NT) {
         Srow[i] = -1;

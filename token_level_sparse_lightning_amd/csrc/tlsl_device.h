@@ -287,4 +287,66 @@ __device__ __forceinline__ void block_scan2(bool a, bool b, int* ra, int* rb, in
     __syncthreads();
 }
 
+// Minimum and maximum of a uint32 over a workgroup of NT threads (every thread
+// gets both).  `scratch` holds 2*NT/64 ints of LDS; ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void block_minmax_u32(uint32_t* lo, uint32_t* hi, int* scratch) {
+    constexpr int NW = NT / 64;
+    const int w = threadIdx.x >> 6, l = lane_id();
+    uint32_t a = *lo, b = *hi;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        a = min(a, (uint32_t)__shfl_xor((int)a, d, 64));
+        b = max(b, (uint32_t)__shfl_xor((int)b, d, 64));
+    }
+    if (l == 0) { scratch[w] = (int)a; scratch[NW + w] = (int)b; }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        a = min(a, (uint32_t)scratch[i]);
+        b = max(b, (uint32_t)scratch[NW + i]);
+    }
+    __syncthreads();
+    *lo = a;
+    *hi = b;
+}
+
+// Exclusive scan of two ints over a workgroup of NT threads, in thread order,
+// with their totals.  `scratch` holds 2*NT/64 ints of LDS; ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void block_scan_int2(int a, int b, int* ea, int* eb, int* ta, int* tb, int* scratch) {
+    constexpr int NW = NT / 64;
+    const int w = threadIdx.x >> 6, l = lane_id();
+    const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+    if (l == 63) { scratch[w] = ia; scratch[NW + w] = ib; }
+    __syncthreads();
+    int ba = 0, bb = 0, sa = 0, sb = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int ca = scratch[i], cb = scratch[NW + i];
+        if (i < w) { ba += ca; bb += cb; }
+        sa += ca; sb += cb;
+    }
+    *ea = ba + ia - a;
+    *eb = bb + ib - b;
+    *ta = sa;
+    *tb = sb;
+    __syncthreads();
+}
+
+// Copies n (>= 1) items with index i in [0, n) from global memory through
+// `store(i, load(i))`, B loads in flight per thread: every load of a batch is
+// issued (indices clamped to n-1, so always in bounds) before any is used.
+template <int NT, int B, class Load, class Store>
+__device__ __forceinline__ void batched_copy(int n, Load load, Store store) {
+    for (int i0 = threadIdx.x; i0 < n; i0 += NT * B) {
+        decltype(load(0)) v[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) v[u] = load(min(i0 + u * NT, n - 1));
+#pragma unroll
+        for (int u = 0; u < B; ++u)
+            if (i0 + u * NT < n) store(i0 + u * NT, v[u]);
+    }
+}
+
 }  // namespace tlsl

@@ -114,7 +114,8 @@ __global__ __launch_bounds__(TT_NT) void topk_threshold_kernel(TopkArgs a) {
         return;
     }
     const float* sc = a.scores + a.row_start[r];
-    for (int j = tid; j < ns; j += TT_NT) skeys[j] = score_key(sc[(size_t)j * stride]);
+    batched_copy<TT_NT, 16>(ns, [&](int j) { return sc[(size_t)j * stride]; },
+                            [&](int j, float v) { skeys[j] = score_key(v); });
     __syncthreads();
     int gt;
     const uint32_t T = block_select_lds<TT_NT>(ns, need, [&](int i, bool* ok) { *ok = true; return skeys[i]; }, hist,
@@ -203,11 +204,11 @@ __global__ __launch_bounds__(TFIN_NT) void topk_final_kernel(TopkArgs a) {
     }
     TopkFinalSmem& s = sh.f;
     const uint2* src = a.buf + (size_t)r * a.cap;
-    for (int i = tid; i < cnt; i += TFIN_NT) {
-        const uint2 e = src[i];
-        s.keys[i] = score_key(__uint_as_float(e.x));
-        s.pos[i] = e.y;
-    }
+    if (cnt > 0)
+        batched_copy<TFIN_NT, 8>(cnt, [&](int i) { return src[i]; }, [&](int i, uint2 e) {
+            s.keys[i] = score_key(__uint_as_float(e.x));
+            s.pos[i] = e.y;
+        });
     for (int i = tid; i < nwords; i += TFIN_NT) s.bitmap[i] = 0u;
     __syncthreads();
     int gt;
