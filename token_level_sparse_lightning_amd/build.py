@@ -26,6 +26,9 @@ HIPCC_FLAGS = [
     "-fPIC",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # private arrays stay in registers: moving them to LDS turned register
+    # prefetches into store-and-wait sequences
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-Wno-unused-command-line-argument",
     f"-I{os.path.join(ROOT, 'include')}",
 ]

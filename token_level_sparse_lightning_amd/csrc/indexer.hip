@@ -70,26 +70,35 @@ struct Idx {
     // the key scale).
     __device__ __forceinline__ static float score(const uint4 (&qf)[HB][NCH], const float (&wv)[HB][4],
                                                   const uint4 (&kf)[4][NCH]) {
-        float part[4];
+        // the HB head blocks are independent accumulation chains, interleaved
+        // step by step; accumulators alternate between two sets so that the
+        // epilogue of key block kb runs while the products of kb+1 are in flight
+        v4f acc[2][HB];
+        auto products = [&](int kb, v4f (&A)[HB]) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            v4f acc[HB];
+            for (int hb = 0; hb < HB; ++hb) A[hb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int hb = 0; hb < HB; ++hb) acc[hb] = M::run(qf[hb], kf[kb], v4f{0.f, 0.f, 0.f, 0.f});
+            for (int st = 0; st < M::STEPS; ++st)
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) A[hb] = M::step(qf[hb], kf[kb], st, A[hb]);
+        };
+        auto epilogue = [&](const v4f (&A)[HB]) {
             float p = 0.f;
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) p = __builtin_fmaf(wv[hb][r], relu(acc[hb][r]), p);
-            part[kb] = p;
-        }
-        // interleave matrix-core and vector work (1 product : 8 vector ops) so
-        // that one wave's epilogue overlaps its next products
-#pragma unroll
-        for (int i = 0; i < 4 * HB * (DT == kF32 ? 4 * NCH : (DT == kBF16 ? NCH : NCH / 2)); ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-        }
+                for (int r = 0; r < 4; ++r) p = __builtin_fmaf(wv[hb][r], relu(A[hb][r]), p);
+            return p;
+        };
+        float part[4];
+        products(0, acc[0]);
+        products(1, acc[1]);
+        part[0] = epilogue(acc[0]);
+        products(2, acc[0]);
+        part[1] = epilogue(acc[1]);
+        products(3, acc[1]);
+        part[2] = epilogue(acc[0]);
+        part[3] = epilogue(acc[1]);
         return reduce_heads_64(part);
     }
 
@@ -304,18 +313,18 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
         const int j = nsub - 1 - it;
         const int cur = it & 1;
         // prefetch the next subtile into registers
+        // (issued unconditionally from clamped rows, pinned ahead of the compute
+        // and stored to LDS after it, so the loads stay in flight meanwhile)
         constexpr int PER = (KT::CHUNKS + PF_NT - 1) / PF_NT;
-        uint4 pre[PER];
-        if (j > 0) {
-#pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                const int ch = tid + u * PF_NT;
-                if (ch < KT::CHUNKS) {
-                    const int r = ch / KT::CPR, off = (ch % KT::CPR) * 16;
-                    pre[u] = *reinterpret_cast<const uint4*>(kb_base + (size_t)((j - 1) * 64 + r) * KT::ROWB + off);
-                }
-            }
-        }
+        static_assert(PER == 1 || PER == 2, "prefetch holds one or two chunks per thread");
+        auto pf_load = [&](int u) {
+            const int ch = min(tid + u * PF_NT, KT::CHUNKS - 1);
+            const int r = ch / KT::CPR, off = (ch % KT::CPR) * 16;
+            return *reinterpret_cast<const uint4*>(kb_base + (size_t)max((j - 1) * 64 + r, 0) * KT::ROWB + off);
+        };
+        const uint4 pre0 = pf_load(0);
+        const uint4 pre1 = PER > 1 ? pf_load(1) : pre0;
+        asm volatile("" ::: "memory");
         uint4 kf[4][NCH];
         frag_from_lds(ktile[cur], kf);
         const int s = j * 64 + l;
@@ -332,15 +341,17 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
                 a.buf[(tok0 + tq[i]) * (size_t)a.cap + slot] = make_uint2(__float_as_uint(sc), (uint32_t)s);
             cntq[i] += __popcll(m);
         }
+        asm volatile("" ::: "memory");
         if (j > 0) {
-#pragma unroll
-            for (int u = 0; u < PER; ++u) {
+            auto pf_store = [&](int u, const uint4& v) {
                 const int ch = tid + u * PF_NT;
                 if (ch < KT::CHUNKS) {
                     const int r = ch / KT::CPR, off = (ch % KT::CPR) * 16;
-                    *reinterpret_cast<uint4*>(ktile[cur ^ 1] + r * KT::STRIDE + off) = pre[u];
+                    *reinterpret_cast<uint4*>(ktile[cur ^ 1] + r * KT::STRIDE + off) = v;
                 }
-            }
+            };
+            pf_store(0, pre0);
+            if (PER > 1) pf_store(1, pre1);
         }
         __syncthreads();
     }

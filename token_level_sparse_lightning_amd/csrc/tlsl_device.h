@@ -44,6 +44,27 @@ struct Mma {
     static constexpr int NCH = ROWB / 64;               // 16-B chunks per lane
     static_assert(ROWB % 64 == 0, "row must split into 4 lane groups of 16-B chunks");
 
+    // matrix-core instructions per product, and the s-th of them on its own
+    // (run() is the sequence of all steps)
+    static constexpr int STEPS = DT == kF32 ? 4 * NCH : (DT == kBF16 ? NCH : NCH / 2);
+
+    __device__ __forceinline__ static v4f step(const uint4* a, const uint4* b, int s, v4f acc) {
+        if constexpr (DT == kF32) {
+            const uint4 x = a[s >> 2], y = b[s >> 2];
+            const uint32_t xa = (s & 3) == 0 ? x.x : (s & 3) == 1 ? x.y : (s & 3) == 2 ? x.z : x.w;
+            const uint32_t ya = (s & 3) == 0 ? y.x : (s & 3) == 1 ? y.y : (s & 3) == 2 ? y.z : y.w;
+            return __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(xa), __uint_as_float(ya), acc, 0, 0, 0);
+        } else if constexpr (DT == kBF16) {
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[s]), __builtin_bit_cast(v8bf, b[s]),
+                                                           acc, 0, 0, 0);
+        } else {
+            const uint4 a0 = a[2 * s], a1 = a[2 * s + 1], b0 = b[2 * s], b1 = b[2 * s + 1];
+            const v8i av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+            const v8i bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+            return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 0, 0, 0);
+        }
+    }
+
     __device__ __forceinline__ static v4f run(const uint4* a, const uint4* b, v4f acc) {
         if constexpr (DT == kF32) {
 #pragma unroll
