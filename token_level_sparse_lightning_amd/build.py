@@ -35,8 +35,11 @@ HIPCC_FLAGS = [
 
 
 # per-source flags: the calibration loop keeps its loop-carried accumulators in
-# VGPRs (the AGPR form makes the compiler rotate them through copies)
-SOURCE_FLAGS = {"measure.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# VGPRs (the AGPR form makes the compiler rotate them through copies); the
+# indexer is scheduled for instruction-level parallelism (measured 2% faster on
+# the fp8 prefill scoring kernel, neutral elsewhere)
+SOURCE_FLAGS = {"measure.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "indexer.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def _hipcc() -> str:

@@ -249,12 +249,27 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
 #pragma unroll
         for (int i = 0; i < QW; ++i) { rc[i] = 0; rth[i] = -INFINITY; }
         const int nsamp = t_last / a.stride + 1;
-        for (int js = 0; js * 64 < nsamp; ++js) {
-            __syncthreads();
-            copy_rows(ktile[0], js * 64 * a.stride, a.stride);
-            __syncthreads();
+        const int nss = (nsamp + 63) / 64;  // sample subtiles
+        __syncthreads();
+        copy_rows(ktile[0], 0, a.stride);
+        __syncthreads();
+        for (int js = 0; js < nss; ++js) {
+            const int cur = js & 1;
+            // the next sample subtile: loaded into registers now, stored to the
+            // other LDS buffer after this one is scored
+            constexpr int SPER = (KT::CHUNKS + PF_NT - 1) / PF_NT;
+            static_assert(SPER == 1 || SPER == 2, "prefetch holds one or two chunks per thread");
+            auto sp_load = [&](int u) {
+                const int ch = min(tid + u * PF_NT, KT::CHUNKS - 1);
+                const int r = ch / KT::CPR, off = (ch % KT::CPR) * 16;
+                const int key = min(((js + 1) * 64 + r) * a.stride, a.n - 1);
+                return *reinterpret_cast<const uint4*>(kb_base + (size_t)key * KT::ROWB + off);
+            };
+            const uint4 sp0 = sp_load(0);
+            const uint4 sp1 = SPER > 1 ? sp_load(1) : sp0;
+            asm volatile("" ::: "memory");
             uint4 kf[4][NCH];
-            frag_from_lds(ktile[0], kf);
+            frag_from_lds(ktile[cur], kf);
             const int s = (js * 64 + l) * a.stride;
             const float ks = (DT == kFP8) ? a.k_scale[tok0 + min(s, a.n - 1)] : 1.f;
 #pragma unroll
@@ -290,6 +305,19 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
                     rth[i] = v;
                 }
             }
+            asm volatile("" ::: "memory");
+            if (js + 1 < nss) {
+                auto sp_store = [&](int u, const uint4& v) {
+                    const int ch = tid + u * PF_NT;
+                    if (ch < KT::CHUNKS) {
+                        const int r = ch / KT::CPR, off = (ch % KT::CPR) * 16;
+                        *reinterpret_cast<uint4*>(ktile[cur ^ 1] + r * KT::STRIDE + off) = v;
+                    }
+                };
+                sp_store(0, sp0);
+                if (SPER > 1) sp_store(1, sp1);
+            }
+            __syncthreads();
         }
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
