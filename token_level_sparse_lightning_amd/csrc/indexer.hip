@@ -192,7 +192,11 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
     __shared__ float rbuf[TQ][PF_RBUF];
     __shared__ uint32_t whist[PF_WAVES][256];
 
-    const int tid = threadIdx.x, wv_id = tid >> 6, l = lane_id(), g = l >> 4, c = l & 15;
+    // the wave index is uniform across the wave: in a scalar register, every
+    // per-query quantity derived from it is scalar too
+    // the wave index is uniform across the wave: in a scalar register, every
+    // per-query quantity derived from it is scalar too
+    const int tid = threadIdx.x, wv_id = __builtin_amdgcn_readfirstlane(tid >> 6), l = lane_id(), g = l >> 4, c = l & 15;
     const int b = blockIdx.x % a.B;
     const int tile = a.tiles - 1 - blockIdx.x / a.B;  // heaviest tiles first
     const int t0 = tile * TQ;
@@ -306,7 +310,7 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
                 }
             }
             asm volatile("" ::: "memory");
-            if (js + 1 < nss) {
+            {
                 auto sp_store = [&](int u, const uint4& v) {
                     const int ch = tid + u * PF_NT;
                     if (ch < KT::CHUNKS) {
@@ -357,20 +361,30 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
         frag_from_lds(ktile[cur], kf);
         const int s = j * 64 + l;
         const float ks = (DT == kFP8) ? a.k_scale[tok0 + min(s, a.n - 1)] : 1.f;
+        // candidate appends are held until the prefetched subtile is in LDS:
+        // a store issued between the prefetch loads and their use would make
+        // the wait for the loads wait for the store as well
+        bool cst[QW];
+        size_t cidx[QW];
+        uint2 cval[QW];
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
+            cst[i] = false;
             if (!qv[i] || j * 64 > tq[i]) continue;
             float sc = I::score(qf[i], wv[i], kf);
             if (DT == kFP8) sc *= ks;
             const bool ok = s <= tq[i] && sc >= theta[i];
             const uint64_t m = ballot(ok);
             const int slot = cntq[i] + rank_above(m);
-            if (ok && slot < a.cap)
-                a.buf[(tok0 + tq[i]) * (size_t)a.cap + slot] = make_uint2(__float_as_uint(sc), (uint32_t)s);
+            cst[i] = ok && slot < a.cap;
+            cidx[i] = (tok0 + tq[i]) * (size_t)a.cap + slot;
+            cval[i] = make_uint2(__float_as_uint(sc), (uint32_t)s);
             cntq[i] += __popcll(m);
         }
         asm volatile("" ::: "memory");
-        if (j > 0) {
+        {
+            // stored on the last trip too (into the idle buffer, never read):
+            // every path then retires the prefetch loads here
             auto pf_store = [&](int u, const uint4& v) {
                 const int ch = tid + u * PF_NT;
                 if (ch < KT::CHUNKS) {
@@ -381,6 +395,9 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
             pf_store(0, pre0);
             if (PER > 1) pf_store(1, pre1);
         }
+#pragma unroll
+        for (int i = 0; i < QW; ++i)
+            if (cst[i]) a.buf[cidx[i]] = cval[i];
         __syncthreads();
     }
     if (l == 0) {
