@@ -410,7 +410,7 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
 // ---------------------------------------------------------------------------
 // Stage 2: exact selection from a row's candidate buffer.
 // ---------------------------------------------------------------------------
-constexpr int FIN_NT = 256;
+constexpr int FIN_NT = 512;
 
 struct FinalizeArgs {
     const uint2* buf;
