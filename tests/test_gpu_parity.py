@@ -26,10 +26,19 @@ F32, BF16, FP8 = synth.DT_F32, synth.DT_BF16, synth.DT_FP8
 # ---------------------------------------------------------------------------
 def _score_rows(seed):
     rng = np.random.default_rng(seed)
-    lens = [0, 1, 5, 63, 64, 65, 100, 1000, 2047, 2048, 2049, 5000, 20000, 20000, 9000]
+    lens = [0, 1, 5, 63, 64, 65, 100, 1000, 2047, 2048, 2049, 5000, 4000, 3500, 20000, 20000, 9000]
     rows = []
     for i, L in enumerate(lens):
-        if i == len(lens) - 3:
+        if i in (len(lens) - 5, len(lens) - 4):
+            # fits the candidate buffer whole: 1500 distinct high scores over a
+            # block of exact ties (+0 and -0 mixed in the second row), so the
+            # selection boundary falls inside a bin of thousands of equal keys
+            r = np.zeros(L, np.float32)
+            hi = rng.choice(L, 1500, replace=False)
+            r[hi] = 5.0 + rng.standard_normal(1500).astype(np.float32)
+            if i == len(lens) - 4:
+                r[r == 0] = np.where(rng.random((r == 0).sum()) < 0.5, -0.0, 0.0)
+        elif i == len(lens) - 3:
             r = np.zeros(L, np.float32)                       # one giant tie
         elif i == len(lens) - 2:
             r = rng.integers(-3, 4, L).astype(np.float32)     # 7 values, huge ties

@@ -422,17 +422,11 @@ struct FinalizeArgs {
     int* fb_list;
 };
 
-constexpr int FIN_BLMAX = 256;  // boundary-bin keys ranked directly
-
 template <int CAPMAX>
 __global__ __launch_bounds__(FIN_NT) void prefill_finalize_kernel(FinalizeArgs a) {
     __shared__ uint32_t fkey[CAPMAX];  // order-preserving keys, ascending position
     __shared__ int fpos[CAPMAX];
-    __shared__ uint32_t hist[2048];
-    __shared__ uint32_t blist[FIN_BLMAX];
-    __shared__ int scratch[64];
-    __shared__ int bcnt, gsh;
-    __shared__ uint32_t tsh;
+    __shared__ SelectSmem sel;
     const int tid = threadIdx.x;
     const int row = blockIdx.x;
     const int t = row % a.n;
@@ -451,77 +445,8 @@ __global__ __launch_bounds__(FIN_NT) void prefill_finalize_kernel(FinalizeArgs a
     __syncthreads();
     uint32_t T = 0u;  // key of the K-th largest candidate
     int gt = cnt;     // candidates with a key above T
-    if (cnt > K) {
-        // one histogram pass over the row's own key span: 2048 bins of 2^s keys
-        uint32_t lo = 0xffffffffu, hi = 0u;
-        for (int i = tid; i < cnt; i += FIN_NT) {
-            lo = min(lo, fkey[i]);
-            hi = max(hi, fkey[i]);
-        }
-        block_minmax_u32<FIN_NT>(&lo, &hi, scratch);
-        const uint32_t span = hi - lo;
-        const int s = span < 2048u ? 0 : (32 - __clz(span)) - 11;
-        for (int i = tid; i < 2048; i += FIN_NT) hist[i] = 0;
-        if (tid == 0) bcnt = 0;
-        __syncthreads();
-        for (int i = tid; i < cnt; i += FIN_NT) atomicAdd(&hist[(fkey[i] - lo) >> s], 1u);
-        __syncthreads();
-        int above;
-        const int d = block_find_bin<FIN_NT, 2048>(hist, K, &above, scratch);
-        const int need = K - above;  // rank of the K-th largest inside bin d
-        const int nb = (int)hist[d];
-        if (s == 0) {
-            T = lo + (uint32_t)d;
-            gt = above;
-        } else if (nb <= FIN_BLMAX) {
-            for (int i = tid; i < cnt; i += FIN_NT) {
-                const uint32_t k = fkey[i];
-                if (((k - lo) >> s) == (uint32_t)d) blist[atomicAdd(&bcnt, 1)] = k;
-            }
-            __syncthreads();
-            // rank the few boundary keys against each other
-            if (tid < nb) {
-                const uint32_t kj = blist[tid];
-                int g = 0, e = 0;
-                for (int m = 0; m < nb; ++m) {
-                    const uint32_t km = blist[m];
-                    g += km > kj;
-                    e += km == kj;
-                }
-                if (g < need && need <= g + e) {  // equal keys write equal values
-                    tsh = kj;
-                    gsh = above + g;
-                }
-            }
-            __syncthreads();
-            T = tsh;
-            gt = gsh;
-        } else {
-            // many candidates in one bin: exact 11/11/10-bit radix over all keys
-            uint32_t prefix = 0, pmask = 0;
-            int left = K;
-            gt = 0;
-            for (int p = 0; p < 3; ++p) {
-                const int sh = radix_shift(p);
-                const uint32_t dm = radix_mask(p);
-                __syncthreads();
-                for (int i = tid; i < 2048; i += FIN_NT) hist[i] = 0;
-                __syncthreads();
-                for (int i = tid; i < cnt; i += FIN_NT) {
-                    const uint32_t key = fkey[i];
-                    if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
-                }
-                __syncthreads();
-                int ab;
-                const int dd = block_find_bin<FIN_NT, 2048>(hist, left, &ab, scratch);
-                gt += ab;
-                left -= ab;
-                prefix |= (uint32_t)dd << sh;
-                pmask |= dm << sh;
-            }
-            T = prefix;
-        }
-    }
+    if (cnt > K)
+        T = block_select_adaptive<FIN_NT>(cnt, K, [&](int i, bool* ok) { *ok = true; return fkey[i]; }, sel, &gt);
     const int need_ties = K - gt;
     int32_t* Srow = a.S + (size_t)row * a.topk;
     float* Ssrow = a.Ss ? a.Ss + (size_t)row * a.topk : nullptr;
@@ -537,7 +462,7 @@ __global__ __launch_bounds__(FIN_NT) void prefill_finalize_kernel(FinalizeArgs a
         ntie += key == T;
     }
     int egt, etie, tgt, ttie;
-    block_scan_int2<FIN_NT>(ngt, ntie, &egt, &etie, &tgt, &ttie, scratch);
+    block_scan_int2<FIN_NT>(ngt, ntie, &egt, &etie, &tgt, &ttie, sel.scratch);
     int slot = egt + min(etie, need_ties);
     int ties_before = etie;
     for (int i = b0; i < b1; ++i) {

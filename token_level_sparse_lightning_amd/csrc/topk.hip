@@ -22,12 +22,12 @@
 
 namespace tlsl {
 
-constexpr int TT_NT = 256;              // threshold workgroup
+constexpr int TT_NT = 1024;             // threshold workgroup
 constexpr int TT_SAMPLE_MAX = 8192;     // sample values held in LDS
 constexpr int TF_NT = 256;              // filter workgroup
 constexpr int TF_PER = 16;              // scores per filter thread
 constexpr int TF_CHUNK = TF_NT * TF_PER;
-constexpr int TFIN_NT = 512;            // final workgroup
+constexpr int TFIN_NT = 1024;           // final workgroup
 constexpr int TSEL_CAPMAX = 8448;       // candidate buffer entries per row, max
 constexpr int TSEL_BITMAP_WORDS = 4096; // rows up to 131072 use the bitmap output
 constexpr int TSEL_CNT_STRIDE = 32;   // one 128-byte line per row counter
@@ -65,42 +65,11 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, int* scratch) 
     return base + incl - v;
 }
 
-// need-th largest (1-based) of key(i) over i < cnt with valid(i), keys in LDS
-// or registers; three radix passes (11, 11, 10 bits).  *gt = count of valid
-// keys strictly above the result.
-template <int NT, class KeyFn>
-__device__ uint32_t block_select_lds(int cnt, int need, KeyFn key_of, uint32_t* hist, int* scratch, int* gt_out) {
-    const int tid = threadIdx.x;
-    uint32_t prefix = 0, pmask = 0;
-    int gt = 0;
-    for (int p = 0; p < 3; ++p) {
-        const int sh = radix_shift(p);
-        const uint32_t dm = radix_mask(p);
-        for (int i = tid; i < 2048; i += NT) hist[i] = 0;
-        __syncthreads();
-        for (int i = tid; i < cnt; i += NT) {
-            bool ok;
-            const uint32_t key = key_of(i, &ok);
-            if (ok && (key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
-        }
-        __syncthreads();
-        int above;
-        const int d = block_find_bin<NT, 2048>(hist, need, &above, scratch);
-        gt += above;
-        need -= above;
-        prefix |= (uint32_t)d << sh;
-        pmask |= dm << sh;
-    }
-    *gt_out = gt;
-    return prefix;
-}
-
 __device__ __forceinline__ int sample_stride(int L) { return max(16, (L + TT_SAMPLE_MAX - 1) / TT_SAMPLE_MAX); }
 
 __global__ __launch_bounds__(TT_NT) void topk_threshold_kernel(TopkArgs a) {
     __shared__ uint32_t skeys[TT_SAMPLE_MAX];
-    __shared__ uint32_t hist[2048];
-    __shared__ int scratch[64];
+    __shared__ SelectSmem sel;
     const int r = blockIdx.x, tid = threadIdx.x;
     const int L = max(a.row_len[r], 0);
     if (tid == 0) a.cnt[r * TSEL_CNT_STRIDE] = 0;
@@ -118,8 +87,8 @@ __global__ __launch_bounds__(TT_NT) void topk_threshold_kernel(TopkArgs a) {
                             [&](int j, float v) { skeys[j] = score_key(v); });
     __syncthreads();
     int gt;
-    const uint32_t T = block_select_lds<TT_NT>(ns, need, [&](int i, bool* ok) { *ok = true; return skeys[i]; }, hist,
-                                               scratch, &gt);
+    const uint32_t T = block_select_adaptive<TT_NT>(ns, need, [&](int i, bool* ok) { *ok = true; return skeys[i]; },
+                                                    sel, &gt);
     if (tid == 0) a.theta[r] = key_score(T);
 }
 
@@ -172,8 +141,8 @@ struct TopkFinalSmem {
     uint32_t keys[TSEL_CAPMAX];
     uint32_t pos[TSEL_CAPMAX];
     uint32_t bitmap[TSEL_BITMAP_WORDS];
-    uint32_t hist[2048];
-    int scratch[64];
+    SelectSmem sel;
+    int nties;
 };
 
 union TopkFinalShared {
@@ -210,15 +179,25 @@ __global__ __launch_bounds__(TFIN_NT) void topk_final_kernel(TopkArgs a) {
             s.pos[i] = e.y;
         });
     for (int i = tid; i < nwords; i += TFIN_NT) s.bitmap[i] = 0u;
+    if (tid == 0) s.nties = 0;
     __syncthreads();
     int gt;
-    const uint32_t T = block_select_lds<TFIN_NT>(cnt, K, [&](int i, bool* ok) { *ok = true; return s.keys[i]; }, s.hist,
-                                                 s.scratch, &gt);
-    // ties at T: keep the (K - gt) lowest positions -> largest inverted position
+    const uint32_t T = block_select_adaptive<TFIN_NT>(cnt, K, [&](int i, bool* ok) { *ok = true; return s.keys[i]; },
+                                                      s.sel, &gt);
+    // ties at T: keep the (K - gt) lowest positions, i.e. the largest inverted
+    // positions; when every tie is kept no selection is needed
     const int need_ties = K - gt;
-    int tgt;
-    const uint32_t inv_cut = block_select_lds<TFIN_NT>(
-        cnt, need_ties, [&](int i, bool* ok) { *ok = s.keys[i] == T; return ~s.pos[i]; }, s.hist, s.scratch, &tgt);
+    int nt_local = 0;
+    for (int i = tid; i < cnt; i += TFIN_NT) nt_local += s.keys[i] == T;
+    nt_local = wave_sum(nt_local);
+    if (lane_id() == 0 && nt_local) atomicAdd(&s.nties, nt_local);
+    __syncthreads();
+    uint32_t inv_cut = 0u;
+    if (s.nties > need_ties) {
+        int tgt;
+        inv_cut = block_select_adaptive<TFIN_NT>(
+            cnt, need_ties, [&](int i, bool* ok) { *ok = s.keys[i] == T; return ~s.pos[i]; }, s.sel, &tgt);
+    }
     for (int i = tid; i < cnt; i += TFIN_NT) {
         const uint32_t key = s.keys[i];
         if (key > T || (key == T && ~s.pos[i] >= inv_cut)) atomicOr(&s.bitmap[s.pos[i] >> 5], 1u << (s.pos[i] & 31));
@@ -230,7 +209,7 @@ __global__ __launch_bounds__(TFIN_NT) void topk_final_kernel(TopkArgs a) {
     int mine = 0;
     for (int wd = w0; wd < w1; ++wd) mine += __popc(s.bitmap[wd]);
     int total;
-    int o = block_excl_scan<TFIN_NT>(mine, &total, s.scratch);
+    int o = block_excl_scan<TFIN_NT>(mine, &total, s.sel.scratch);
     for (int wd = w0; wd < w1; ++wd) {
         uint32_t bits = s.bitmap[wd];
         while (bits) {

@@ -20,6 +20,120 @@ struct TopkSmem {
 __device__ __forceinline__ int radix_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
 __device__ __forceinline__ uint32_t radix_mask(int p) { return p == 2 ? 0x3ffu : 0x7ffu; }
 
+// ---------------------------------------------------------------------------
+// need-th largest (1 <= need <= number of valid keys) of key_of(i, &valid),
+// i < cnt, over a workgroup of NT threads; key_of reads workgroup-visible
+// memory and is called up to three times per index.  Returns the key T and
+// *gt = number of valid keys above T.
+//
+// One histogram pass over the keys' own span [lo, hi] (2048 bins of 2^s keys)
+// finds the bin holding the result; the few keys of that bin are then ranked
+// against each other.  A bin with more than SEL_BLMAX keys (a span dominated
+// by near-equal keys) falls back to three radix passes over the full key.
+// exact = false stops after the histogram and returns the bin's lower edge, a
+// lower bound of the need-th largest key (*gt is then not set); the bound is
+// loose when the span is wide (2048 bins over keys of both signs).
+// Ends with a barrier, so `sm` may be reused right away.
+// ---------------------------------------------------------------------------
+constexpr int SEL_BLMAX = 256;
+
+struct SelectSmem {
+    uint32_t hist[2048];
+    uint32_t blist[SEL_BLMAX];
+    int scratch[64];
+    int bcnt, gsh;
+    uint32_t tsh;
+};
+
+template <int NT, class KeyFn>
+__device__ uint32_t block_select_adaptive(int cnt, int need, KeyFn key_of, SelectSmem& sm, int* gt_out,
+                                          bool exact = true) {
+    const int tid = threadIdx.x;
+    uint32_t lo = 0xffffffffu, hi = 0u;
+    for (int i = tid; i < cnt; i += NT) {
+        bool ok;
+        const uint32_t k = key_of(i, &ok);
+        if (ok) {
+            lo = min(lo, k);
+            hi = max(hi, k);
+        }
+    }
+    block_minmax_u32<NT>(&lo, &hi, sm.scratch);
+    const uint32_t span = hi - lo;
+    const int s = span < 2048u ? 0 : (32 - __clz(span)) - 11;
+    for (int i = tid; i < 2048; i += NT) sm.hist[i] = 0;
+    if (tid == 0) sm.bcnt = 0;
+    __syncthreads();
+    for (int i = tid; i < cnt; i += NT) {
+        bool ok;
+        const uint32_t k = key_of(i, &ok);
+        if (ok) atomicAdd(&sm.hist[(k - lo) >> s], 1u);
+    }
+    __syncthreads();
+    int above;
+    const int d = block_find_bin<NT, 2048>(sm.hist, need, &above, sm.scratch);
+    const uint32_t edge = lo + ((uint32_t)d << s);
+    if (!exact) return edge;
+    const int nb = (int)sm.hist[d];
+    const int rank = need - above;  // inside bin d
+    __syncthreads();  // every thread holds nb before the fallback clears hist
+    uint32_t T;
+    int gt;
+    if (s == 0) {
+        T = edge;
+        gt = above;
+    } else if (nb <= SEL_BLMAX) {
+        for (int i = tid; i < cnt; i += NT) {
+            bool ok;
+            const uint32_t k = key_of(i, &ok);
+            if (ok && ((k - lo) >> s) == (uint32_t)d) sm.blist[atomicAdd(&sm.bcnt, 1)] = k;
+        }
+        __syncthreads();
+        if (tid < nb) {
+            const uint32_t kj = sm.blist[tid];
+            int g = 0, e = 0;
+            for (int m = 0; m < nb; ++m) {
+                const uint32_t km = sm.blist[m];
+                g += km > kj;
+                e += km == kj;
+            }
+            if (g < rank && rank <= g + e) {  // equal keys write equal values
+                sm.tsh = kj;
+                sm.gsh = above + g;
+            }
+        }
+        __syncthreads();
+        T = sm.tsh;
+        gt = sm.gsh;
+    } else {
+        uint32_t prefix = 0, pmask = 0;
+        int left = need;
+        gt = 0;
+        for (int p = 0; p < 3; ++p) {
+            const int sh = radix_shift(p);
+            const uint32_t dm = radix_mask(p);
+            for (int i = tid; i < 2048; i += NT) sm.hist[i] = 0;
+            __syncthreads();
+            for (int i = tid; i < cnt; i += NT) {
+                bool ok;
+                const uint32_t k = key_of(i, &ok);
+                if (ok && (k & pmask) == prefix) atomicAdd(&sm.hist[(k >> sh) & dm], 1u);
+            }
+            __syncthreads();
+            int ab;
+            const int dd = block_find_bin<NT, 2048>(sm.hist, left, &ab, sm.scratch);
+            gt += ab;
+            left -= ab;
+            prefix |= (uint32_t)dd << sh;
+            pmask |= dm << sh;
+        }
+        T = prefix;
+    }
+    __syncthreads();
+    *gt_out = gt;
+    return T;
+}
+
 // Exact selection of the K = min(k, L) best of sc[0..L) ordered by (score desc,
 // position asc).  Writes S[0..k): the selected positions ascending, then -1;
 // Ss (optional): each slot's score, -inf for unused slots.  All NT threads of
