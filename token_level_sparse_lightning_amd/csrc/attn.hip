@@ -351,20 +351,48 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             for (int ch = 0; ch < NCP; ++ch) o[db] = mma_chunk(vb[db][ch], pf[ch], o[db]);
         }
     };
-    Pre P;
-    if (ntl > 0) {
-        load_tile(tlist[0], P);
-        store_tile(P);
-    }
-    __syncthreads();
-    for (int ti = 0; ti < ntl; ++ti) {
-        load_tile(tlist[min(ti + 1, ntl - 1)], P);
-        asm volatile("" ::: "memory");
-        compute(tlist[ti]);
+    if constexpr (!DECODE) {
+        // prefill: the gathered rows are mostly cache-resident; one tile ahead
+        Pre P;
+        if (ntl > 0) {
+            load_tile(tlist[0], P);
+            store_tile(P);
+        }
         __syncthreads();
-        if (ti + 1 >= ntl) break;
-        store_tile(P);
+        for (int ti = 0; ti < ntl; ++ti) {
+            load_tile(tlist[min(ti + 1, ntl - 1)], P);
+            asm volatile("" ::: "memory");
+            compute(tlist[ti]);
+            __syncthreads();
+            if (ti + 1 >= ntl) break;
+            store_tile(P);
+            __syncthreads();
+        }
+    } else {
+        // decode: cold rows from a large cache; two tiles in flight
+        Pre P0, P1;
+        if (ntl > 0) {
+            load_tile(tlist[0], P0);
+            store_tile(P0);
+            load_tile(tlist[min(1, ntl - 1)], P0);
+        }
         __syncthreads();
+        for (int ti = 0; ti < ntl; ti += 2) {
+            load_tile(tlist[min(ti + 2, ntl - 1)], P1);
+            asm volatile("" ::: "memory");
+            compute(tlist[ti]);
+            __syncthreads();
+            if (ti + 1 >= ntl) break;
+            store_tile(P0);
+            __syncthreads();
+            load_tile(tlist[min(ti + 3, ntl - 1)], P0);
+            asm volatile("" ::: "memory");
+            compute(tlist[ti + 1]);
+            __syncthreads();
+            if (ti + 2 >= ntl) break;
+            store_tile(P1);
+            __syncthreads();
+        }
     }
 
     // ---- finish --------------------------------------------------------------

@@ -102,6 +102,31 @@ struct Idx {
         return reduce_heads_64(part);
     }
 
+    // The same scores with one accumulator set (fewer registers, more waves
+    // per SIMD; for the bandwidth-bound scan).  Identical summation order, so
+    // the results are bit-identical to score().
+    __device__ __forceinline__ static float score_lean(const uint4 (&qf)[HB][NCH], const float (&wv)[HB][4],
+                                                       const uint4 (&kf)[4][NCH]) {
+        float part[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            v4f acc[HB];
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) acc[hb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < M::STEPS; ++st)
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) acc[hb] = M::step(qf[hb], kf[kb], st, acc[hb]);
+            float p = 0.f;
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) p = __builtin_fmaf(wv[hb][r], relu(acc[hb][r]), p);
+            part[kb] = p;
+        }
+        return reduce_heads_64(part);
+    }
+
     // Key fragments of keys key0 + 16*kb + (l & 15), rows clamped to last,
     // straight from global memory.
     __device__ __forceinline__ static void load_keys_global(const unsigned char* kbase, int key0, int last,
@@ -667,7 +692,7 @@ __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned cha
             // the compiler to wait for every outstanding load before using ks
             I::load_keys_global(kbase, min(ka, L - 1), L - 1, kf[1]);
             {
-                const float s = I::score(qf, wv, kf[0]) * ks;
+                const float s = I::score_lean(qf, wv, kf[0]) * ks;
                 if (key0 + l < L) scores[start + key0 + l] = s;
             }
             g = ga;
@@ -678,7 +703,7 @@ __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned cha
             const int kbk = key0 + 64 * NWV;
             I::load_keys_global(kbase, min(kbk, L - 1), L - 1, kf[0]);
             {
-                const float s = I::score(qf, wv, kf[1]) * ks;
+                const float s = I::score_lean(qf, wv, kf[1]) * ks;
                 if (key0 + l < L) scores[start + key0 + l] = s;
             }
             g = gb;
