@@ -31,6 +31,8 @@ constexpr int AT_TS = 32;      // slots per tile
 constexpr int AT_KMAX = 4096;  // slots per workgroup (k <= 4096)
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 // two floats to packed bf16 (round to nearest even; one gfx950 instruction)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -76,7 +78,9 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     // rows 16 apart are shifted by 64 bytes so that the 16 rows one lane
     // group reads for the logits fall in distinct banks
     __shared__ __align__(16) unsigned char ctile[AT_TS * CSTR + (AT_TS / 16) * 64];
-    __shared__ __align__(16) unsigned char vt[DV * VSTR];
+    // fp32 values are also kept transposed ([d][slot]) for the P.V product;
+    // bf16 values are read transposed from ctile by the LDS transpose load
+    __shared__ __align__(16) unsigned char vt[EB == 2 ? 16 : DV * VSTR];
     __shared__ __align__(16) int slots[AT_KMAX];  // the row's slot range: position or -1
     __shared__ int tile_any[AT_KMAX / AT_TS];
     __shared__ int tlist[AT_KMAX / AT_TS];
@@ -165,9 +169,11 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     constexpr int RC = (DQK - DV) / VPC;  // position-part chunks per row
     constexpr int RITEMS = AT_TS * RC;
     constexpr int RPER = (RITEMS + NT - 1) / NT;
+    // plain 4 x u32 vectors: copied with vector loads and stores (a struct
+    // copy would go through a stack slot)
     struct Pre {
-        uint4 v[VPER][4];
-        uint4 r[RPER > 0 ? RPER : 1];
+        v4u v[VPER][4];
+        v4u r[RPER > 0 ? RPER : 1];
     };
     // each thread gathers the same (slot quad, chunk) items of every tile:
     // their base addresses are fixed, a load adds the slot's entry offset
@@ -200,13 +206,13 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
                 // an invalid slot reads the row's entry 0 (always in bounds):
                 // its logit is masked to -inf, so its probability is exactly 0
                 const uint32_t pos = (uint32_t)max(qs[u], 0);
-                P.v[j][u] = *reinterpret_cast<const uint4*>(vsrc[j] + (size_t)pos * CROW);
+                P.v[j][u] = *reinterpret_cast<const v4u*>(vsrc[j] + (size_t)pos * CROW);
             }
         }
 #pragma unroll
         for (int j = 0; j < RPER; ++j) {
             const uint32_t pos = (uint32_t)max(sl[rrow[j]], 0);
-            P.r[j] = *reinterpret_cast<const uint4*>(rsrc[j] + (size_t)pos * CROW);
+            P.r[j] = *reinterpret_cast<const v4u*>(rsrc[j] + (size_t)pos * CROW);
         }
     };
     auto store_tile = [&](const Pre& P) {
@@ -216,25 +222,12 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             if (it < VITEMS) {
                 const int qd = it % (AT_TS / 4), oc = it / (AT_TS / 4);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(ctile + crow(4 * qd + u) + oc * 16) = P.v[j][u];
-                if constexpr (EB == 2) {
-                    const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&P.v[j][0]);
-                    const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&P.v[j][1]);
-                    const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&P.v[j][2]);
-                    const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&P.v[j][3]);
-#pragma unroll
-                    for (int i = 0; i < VPC; ++i) {
-                        uint2 pk = make_uint2((uint32_t)e0[i] | ((uint32_t)e1[i] << 16), (uint32_t)e2[i] | ((uint32_t)e3[i] << 16));
-                        *reinterpret_cast<uint2*>(vt + (oc * VPC + i) * VSTR + 4 * qd * EB) = pk;
-                    }
-                } else {
-                    const uint32_t* e0 = reinterpret_cast<const uint32_t*>(&P.v[j][0]);
-                    const uint32_t* e1 = reinterpret_cast<const uint32_t*>(&P.v[j][1]);
-                    const uint32_t* e2 = reinterpret_cast<const uint32_t*>(&P.v[j][2]);
-                    const uint32_t* e3 = reinterpret_cast<const uint32_t*>(&P.v[j][3]);
+                for (int u = 0; u < 4; ++u) *reinterpret_cast<v4u*>(ctile + crow(4 * qd + u) + oc * 16) = P.v[j][u];
+                if constexpr (EB == 4) {
 #pragma unroll
                     for (int i = 0; i < VPC; ++i)
-                        *reinterpret_cast<uint4*>(vt + (oc * VPC + i) * VSTR + 4 * qd * EB) = make_uint4(e0[i], e1[i], e2[i], e3[i]);
+                        *reinterpret_cast<v4u*>(vt + (oc * VPC + i) * VSTR + 4 * qd * EB) =
+                            v4u{P.v[j][0][i], P.v[j][1][i], P.v[j][2][i], P.v[j][3][i]};
                 }
             }
         }
@@ -243,7 +236,7 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             const int it = tid + j * NT;
             if (it < RITEMS) {
                 const int r = it / RC, oc = DV / VPC + it % RC;
-                *reinterpret_cast<uint4*>(ctile + crow(r) + oc * 16) = P.r[j];
+                *reinterpret_cast<v4u*>(ctile + crow(r) + oc * 16) = P.r[j];
             }
         }
     };
@@ -302,11 +295,29 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
         // V^T fragments of the tile, read before the softmax so that their
         // latency overlaps it
         uint4 vb[NDB][NCP];
+        if constexpr (EB == 2) {
+            // transpose loads from the row-major tile: within each 16-lane
+            // group, lane r addresses row (slot) s0 + r/4 at dims d0 + 4*(r%4)
+            // .. +3, and lane i receives slots s0..s0+3 of dim d0 + i; two
+            // loads (s0 = 8g, 8g+4) give the lane's 8-slot fragment
+            const int rr = l & 15;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            const uint4* vp = reinterpret_cast<const uint4*>(vt + (half * DVW + 16 * db + c) * VSTR + g * (VROW / 4));
+            for (int db = 0; db < NDB; ++db) {
+                const int d0 = half * DVW + 16 * db;
+                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4s*)(ctile + crow(8 * g + (rr >> 2)) + (d0 + 4 * (rr & 3)) * 2));
+                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4s*)(ctile + crow(8 * g + 4 + (rr >> 2)) + (d0 + 4 * (rr & 3)) * 2));
+                const uint2 a = __builtin_bit_cast(uint2, lo), b2 = __builtin_bit_cast(uint2, hi);
+                vb[db][0] = make_uint4(a.x, a.y, b2.x, b2.y);
+            }
+        } else {
 #pragma unroll
-            for (int ch = 0; ch < NCP; ++ch) vb[db][ch] = vp[ch];
+            for (int db = 0; db < NDB; ++db) {
+                const uint4* vp = reinterpret_cast<const uint4*>(vt + (half * DVW + 16 * db + c) * VSTR + g * (VROW / 4));
+#pragma unroll
+                for (int ch = 0; ch < NCP; ++ch) vb[db][ch] = vp[ch];
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         // ---- online softmax per head -----------------------------------------
