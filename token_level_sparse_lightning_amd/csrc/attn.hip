@@ -77,7 +77,11 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     auto crow = [](int r) { return r * CSTR + (r >> 4) * 64; };
     // rows 16 apart are shifted by 64 bytes so that the 16 rows one lane
     // group reads for the logits fall in distinct banks
-    __shared__ __align__(16) unsigned char ctile[AT_TS * CSTR + (AT_TS / 16) * 64];
+    // bf16 (wave pairs): two tile buffers, the next tile is stored while this
+    // one is processed; fp32: one buffer
+    constexpr int NBUF = DSPLIT > 1 ? 2 : 1;
+    constexpr int CTB = AT_TS * CSTR + (AT_TS / 16) * 64;  // bytes of one tile buffer
+    __shared__ __align__(16) unsigned char ctile[NBUF][CTB];
     // fp32 values are also kept transposed ([d][slot]) for the P.V product;
     // bf16 values are read transposed from ctile by the LDS transpose load
     __shared__ __align__(16) unsigned char vt[EB == 2 ? 16 : DV * VSTR];
@@ -215,14 +219,14 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             P.r[j] = *reinterpret_cast<const v4u*>(rsrc[j] + (size_t)pos * CROW);
         }
     };
-    auto store_tile = [&](const Pre& P) {
+    auto store_tile = [&](const Pre& P, unsigned char* ct) {
 #pragma unroll
         for (int j = 0; j < VPER; ++j) {
             const int it = tid + j * NT;
             if (it < VITEMS) {
                 const int qd = it % (AT_TS / 4), oc = it / (AT_TS / 4);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) *reinterpret_cast<v4u*>(ctile + crow(4 * qd + u) + oc * 16) = P.v[j][u];
+                for (int u = 0; u < 4; ++u) *reinterpret_cast<v4u*>(ct + crow(4 * qd + u) + oc * 16) = P.v[j][u];
                 if constexpr (EB == 4) {
 #pragma unroll
                     for (int i = 0; i < VPC; ++i)
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             const int it = tid + j * NT;
             if (it < RITEMS) {
                 const int r = it / RC, oc = DV / VPC + it % RC;
-                *reinterpret_cast<v4u*>(ctile + crow(r) + oc * 16) = P.r[j];
+                *reinterpret_cast<v4u*>(ct + crow(r) + oc * 16) = P.r[j];
             }
         }
     };
@@ -255,14 +259,16 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     // the tile being computed sits in LDS while the next one is in flight into
     // registers (loads are unconditional -- past the end they repeat the last
     // tile -- so the compiler's wait counts stay exact)
-    auto compute = [&](int tcur) {
+    // `mid` runs inside the tile's compute, after the P.V fragments are read
+    // and before the P.V products (the next tile's LDS store goes there)
+    auto compute = [&](int tcur, const unsigned char* ct, auto&& mid) {
         const int* sl = slots + tcur * AT_TS;
 
         // ---- logits: Z^T[slot][head]; lane (g,c) gets slots 8g..8g+7 of head c
         float z[8];
         {
-            const uint4* cp0 = reinterpret_cast<const uint4*>(ctile + crow(8 * (c >> 2) + (c & 3)) + (kd0 + g * (QKD / 4)) * EB);
-            const uint4* cp1 = reinterpret_cast<const uint4*>(ctile + crow(8 * (c >> 2) + 4 + (c & 3)) + (kd0 + g * (QKD / 4)) * EB);
+            const uint4* cp0 = reinterpret_cast<const uint4*>(ct + crow(8 * (c >> 2) + (c & 3)) + (kd0 + g * (QKD / 4)) * EB);
+            const uint4* cp1 = reinterpret_cast<const uint4*>(ct + crow(8 * (c >> 2) + 4 + (c & 3)) + (kd0 + g * (QKD / 4)) * EB);
             uint4 ca[NCQ], cb[NCQ];
 #pragma unroll
             for (int ch = 0; ch < NCQ; ++ch) {
@@ -305,9 +311,9 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             for (int db = 0; db < NDB; ++db) {
                 const int d0 = half * DVW + 16 * db;
                 const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4s*)(ctile + crow(8 * g + (rr >> 2)) + (d0 + 4 * (rr & 3)) * 2));
+                    (lds_v4s*)(ct + crow(8 * g + (rr >> 2)) + (d0 + 4 * (rr & 3)) * 2));
                 const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4s*)(ctile + crow(8 * g + 4 + (rr >> 2)) + (d0 + 4 * (rr & 3)) * 2));
+                    (lds_v4s*)(ct + crow(8 * g + 4 + (rr >> 2)) + (d0 + 4 * (rr & 3)) * 2));
                 const uint2 a = __builtin_bit_cast(uint2, lo), b2 = __builtin_bit_cast(uint2, hi);
                 vb[db][0] = make_uint4(a.x, a.y, b2.x, b2.y);
             }
@@ -355,6 +361,7 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             pf[0] = make_uint4(__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]), __float_as_uint(p[3]));
             pf[1] = make_uint4(__float_as_uint(p[4]), __float_as_uint(p[5]), __float_as_uint(p[6]), __float_as_uint(p[7]));
         }
+        mid();
         // ---- O^T[d][head] += V^T[d][slots] P^T[slots][head] -------------------
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -362,46 +369,68 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             for (int ch = 0; ch < NCP; ++ch) o[db] = mma_chunk(vb[db][ch], pf[ch], o[db]);
         }
     };
-    if constexpr (!DECODE) {
-        // prefill: the gathered rows are mostly cache-resident; one tile ahead
+    auto none = [] {};
+    if constexpr (NBUF == 1) {
+        // one buffer: compute, then store the next tile
         Pre P;
         if (ntl > 0) {
             load_tile(tlist[0], P);
-            store_tile(P);
+            store_tile(P, ctile[0]);
         }
         __syncthreads();
         for (int ti = 0; ti < ntl; ++ti) {
             load_tile(tlist[min(ti + 1, ntl - 1)], P);
             asm volatile("" ::: "memory");
-            compute(tlist[ti]);
+            compute(tlist[ti], ctile[0], none);
             __syncthreads();
             if (ti + 1 >= ntl) break;
-            store_tile(P);
+            store_tile(P, ctile[0]);
+            __syncthreads();
+        }
+    } else if constexpr (!DECODE) {
+        // prefill (rows mostly cache-resident): one tile ahead in registers;
+        // it is stored into the idle buffer during this tile's compute (every
+        // read of that buffer ended before the last barrier)
+        Pre P;
+        if (ntl > 0) {
+            load_tile(tlist[0], P);
+            store_tile(P, ctile[0]);
+        }
+        __syncthreads();
+        for (int ti = 0; ti < ntl; ++ti) {
+            const bool more = ti + 1 < ntl;
+            load_tile(tlist[min(ti + 1, ntl - 1)], P);
+            asm volatile("" ::: "memory");
+            compute(tlist[ti], ctile[ti & 1], [&] {
+                asm volatile("" ::: "memory");
+                if (more) store_tile(P, ctile[(ti + 1) & 1]);
+            });
             __syncthreads();
         }
     } else {
-        // decode: cold rows from a large cache; two tiles in flight
+        // decode (cold rows from a large cache): two tiles ahead in registers
         Pre P0, P1;
         if (ntl > 0) {
             load_tile(tlist[0], P0);
-            store_tile(P0);
+            store_tile(P0, ctile[0]);
             load_tile(tlist[min(1, ntl - 1)], P0);
         }
         __syncthreads();
         for (int ti = 0; ti < ntl; ti += 2) {
             load_tile(tlist[min(ti + 2, ntl - 1)], P1);
             asm volatile("" ::: "memory");
-            compute(tlist[ti]);
+            compute(tlist[ti], ctile[0], [&] {
+                asm volatile("" ::: "memory");
+                if (ti + 1 < ntl) store_tile(P0, ctile[1]);
+            });
             __syncthreads();
             if (ti + 1 >= ntl) break;
-            store_tile(P0);
-            __syncthreads();
             load_tile(tlist[min(ti + 3, ntl - 1)], P0);
             asm volatile("" ::: "memory");
-            compute(tlist[ti + 1]);
-            __syncthreads();
-            if (ti + 2 >= ntl) break;
-            store_tile(P1);
+            compute(tlist[ti + 1], ctile[1], [&] {
+                asm volatile("" ::: "memory");
+                if (ti + 2 < ntl) store_tile(P1, ctile[0]);
+            });
             __syncthreads();
         }
     }
