@@ -314,15 +314,16 @@ def cpu_baseline(inp, k, n, target_s=15.0):
 # HBM traffic of the headline kernel per launch, from two rocprofv3 --pmc runs of
 # `bench.py --no-cpu --only decode --steps 3 --warmup 1` (FETCH_SIZE, then WRITE_SIZE,
 # KiB per dispatch, averaged over the dispatches of the kernel), each scaled by
-# the same counter's reading for the 1 GiB calibration copy in the same run.
+# the same counter's reading for the 1 GiB calibration copy (the reading that
+# counts the copy's writes exactly; see profiles/prefill_score_kernel_bf16_n8192.md).
 # The figures hold only for the kernel sources they were taken on: when the
 # hash of those sources differs, the traffic is reported as null.
 TRAFFIC_SOURCES = ("indexer.hip", "tlsl_device.h", "tlsl_internal.h", "topk_common.h")
 TRAFFIC = {
     # profiles/prefill_score_kernel_bf16_n8192.md
     "prefill_score_kernel": {
-        "sources_sha256": "0630367581304d9ab55726599604a7024885ab61d72bc9d0dea531b2327bbca8",
-        "fetch_kib": 85971.4688, "write_kib": 158375.2266,
+        "sources_sha256": "c7617df54d24104bacbd647582c90ba9ac47b89a157cd5ea582daca0a30d3ad4",
+        "fetch_kib": 85483.1719, "write_kib": 158355.9453,
         "copy_fetch_kib": 524313.5357, "copy_write_kib": 1048576.0, "copy_bytes": 1 << 30,
     },
 }
