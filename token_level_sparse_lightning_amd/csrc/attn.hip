@@ -11,11 +11,12 @@
 // through LDS) and the output O^T = V^T P^T over the value dims -- so each wave
 // holds part of a query fragment and part of an output accumulator in
 // registers, leaving room to keep the next tile's rows in flight.  Per tile of
-// 32 slots the selected rows are gathered once into LDS, twice laid out:
-// row-major [slot][Dqk] (A operand of Z^T) and transposed [Dv][slot] (A operand
-// of O^T), so both products read 16-byte fragments; the slot order inside the
-// first product is permuted so that each lane's probabilities are exactly the
-// P^T fragment the second product needs.  Softmax is online (running max and
+// 32 slots the selected rows are gathered once into LDS, row-major
+// [slot][Dqk]: the A operand of Z^T is read from it directly and, for bf16,
+// the A operand of O^T (V^T) with the LDS transpose load; fp32 keeps a second,
+// transposed [Dv][slot] copy.  The slot order inside the first product is
+// permuted so that each lane's probabilities are exactly the P^T fragment the
+// second product needs.  Softmax is online (running max and
 // sum per head, base-2 exponentials with log2(e) folded into the scale).  When
 // a row needs two head groups, their workgroups are numbered 8 apart so that
 // they run on the same XCD and the second gather of each row is served by that
@@ -69,18 +70,32 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     constexpr int NDB = DVW / 16;             // output dim blocks per wave
     constexpr int NCP = AT_TS * EB / 64;      // chunks per lane of a P^T / V^T fragment
     constexpr int CROW = DQK * EB;            // bytes of one entry
-    constexpr int CSTR = CROW + 16;           // padded LDS row
     constexpr int VROW = AT_TS * EB;          // bytes of one transposed value row
     constexpr int VSTR = VROW + 16;           // 16-byte aligned rows for the 16-byte fragment reads
     constexpr int VPC = 16 / EB;              // values per 16-B chunk
     static_assert((QKD * EB) % 64 == 0 && DVW % 16 == 0 && DV <= DQK, "shape");
-    auto crow = [](int r) { return r * CSTR + (r >> 4) * 64; };
-    // rows 16 apart are shifted by 64 bytes so that the 16 rows one lane
-    // group reads for the logits fall in distinct banks
+    // LDS tile rows.  bf16: unpadded rows of 72 16-byte chunks; chunk k of
+    // row r sits at chunk k ^ f(r) of its group of 16 (the last 8 chunks:
+    // k ^ f(r)/2 inside those 8), f(r) = 4*(r/8) + r%4.  The 16 rows one lane
+    // group reads for the logits have f = 0..15 and so do the rows of one
+    // transpose load, so both reads, and the 16 (slot, chunk) items of one
+    // store, fall in distinct banks.  fp32: padded rows, those 16 apart
+    // shifted by 64 bytes.
+    static_assert(EB == 4 || CROW == 72 * 16, "bf16 tile layout assumes 576-wide entries");
+    constexpr int CSTR = EB == 2 ? CROW : CROW + 16;
+    auto cpos = [](int r, int k) -> int {  // byte offset of chunk k of row r
+        if constexpr (EB == 2) {
+            const int f = ((r >> 3) << 2) | (r & 3);
+            const int kk = k < 64 ? ((k & ~15) | ((k ^ f) & 15)) : (64 | ((k ^ (f >> 1)) & 7));
+            return r * CSTR + 16 * kk;
+        } else {
+            return r * CSTR + (r >> 4) * 64 + 16 * k;
+        }
+    };
     // bf16 (wave pairs): two tile buffers, the next tile is stored while this
     // one is processed; fp32: one buffer
     constexpr int NBUF = DSPLIT > 1 ? 2 : 1;
-    constexpr int CTB = AT_TS * CSTR + (AT_TS / 16) * 64;  // bytes of one tile buffer
+    constexpr int CTB = AT_TS * CSTR + (EB == 2 ? 0 : (AT_TS / 16) * 64);  // bytes of one tile buffer
     __shared__ __align__(16) unsigned char ctile[NBUF][CTB];
     // fp32 values are also kept transposed ([d][slot]) for the P.V product;
     // bf16 values are read transposed from ctile by the LDS transpose load
@@ -185,13 +200,27 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     int vqd[VPER], rrow[RPER > 0 ? RPER : 1];
     const unsigned char* vsrc[VPER];
     const unsigned char* rsrc[RPER > 0 ? RPER : 1];
+    // value item -> (slot quad, chunk).  bf16: within 16 lanes, 4 consecutive
+    // chunks x 4 quads whose rows differ in f (conflict-free stores; 64-byte
+    // runs per entry in the gather); fp32: the quad varies fastest
+    auto vitem = [](int it, int& qd, int& oc) {
+        if constexpr (EB == 2) {
+            static_assert(VITEMS == 512, "bf16 value items");
+            qd = (((it >> 2) & 3) << 1) | ((it >> 4) & 1);
+            oc = ((it >> 5) << 2) | (it & 3);
+        } else {
+            qd = it % (AT_TS / 4);
+            oc = it / (AT_TS / 4);
+        }
+    };
 #pragma unroll
     for (int j = 0; j < VPER; ++j) {
         // items past the end repeat the last one, so every thread issues the
         // same loads and the compiler's wait counts stay exact
-        const int it = min(tid + j * NT, VITEMS - 1);
-        vqd[j] = it % (AT_TS / 4);  // slot quad varies fastest across lanes
-        vsrc[j] = kvrow + (it / (AT_TS / 4)) * 16;
+        int qd, oc;
+        vitem(min(tid + j * NT, VITEMS - 1), qd, oc);
+        vqd[j] = qd;
+        vsrc[j] = kvrow + oc * 16;
     }
 #pragma unroll
     for (int j = 0; j < RPER; ++j) {
@@ -224,9 +253,10 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
         for (int j = 0; j < VPER; ++j) {
             const int it = tid + j * NT;
             if (it < VITEMS) {
-                const int qd = it % (AT_TS / 4), oc = it / (AT_TS / 4);
+                int qd, oc;
+                vitem(it, qd, oc);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) *reinterpret_cast<v4u*>(ct + crow(4 * qd + u) + oc * 16) = P.v[j][u];
+                for (int u = 0; u < 4; ++u) *reinterpret_cast<v4u*>(ct + cpos(4 * qd + u, oc)) = P.v[j][u];
                 if constexpr (EB == 4) {
 #pragma unroll
                     for (int i = 0; i < VPC; ++i)
@@ -240,10 +270,28 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             const int it = tid + j * NT;
             if (it < RITEMS) {
                 const int r = it / RC, oc = DV / VPC + it % RC;
-                *reinterpret_cast<v4u*>(ct + crow(r) + oc * 16) = P.r[j];
+                *reinterpret_cast<v4u*>(ct + cpos(r, oc)) = P.r[j];
             }
         }
     };
+    // per-lane LDS offsets of the fragment reads (the same in every tile)
+    // logits: chunk (kd0 + g*QKD/4)*EB/16 + ch of row sigma = 8*(c/4) + c%4
+    int qoff[NCQ];
+    const int sig = 8 * (c >> 2) + (c & 3);
+#pragma unroll
+    for (int ch = 0; ch < NCQ; ++ch) qoff[ch] = cpos(sig, (kd0 + g * (QKD / 4)) * EB / 16 + ch);
+    // bf16 transpose loads: lane r of a 16-lane group addresses row 8g + r/4
+    // at dims d0 + 4*(r%4) .. +3, d0 = half*DVW + 16*db
+    int poff[8];
+    if constexpr (EB == 2) {
+        static_assert(NDB == 16, "bf16 value blocks");
+        const int rr = l & 15;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const int d = half * DVW + 16 * db + 4 * (rr & 3);
+            poff[db] = cpos(8 * g + (rr >> 2), d / 8) + 2 * (d & 7);
+        }
+    }
     // one 16-byte chunk of the reduction dimension through the matrix cores
     auto mma_chunk = [](const uint4& x, const uint4& y, v4f acc) -> v4f {
         if constexpr (DT == kBF16) {
@@ -267,13 +315,13 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
         // ---- logits: Z^T[slot][head]; lane (g,c) gets slots 8g..8g+7 of head c
         float z[8];
         {
-            const uint4* cp0 = reinterpret_cast<const uint4*>(ct + crow(8 * (c >> 2) + (c & 3)) + (kd0 + g * (QKD / 4)) * EB);
-            const uint4* cp1 = reinterpret_cast<const uint4*>(ct + crow(8 * (c >> 2) + 4 + (c & 3)) + (kd0 + g * (QKD / 4)) * EB);
+            // rows sigma = 8*(c/4) + c%4 and sigma + 4: the same f (bf16) and the
+            // same 16-row shift (fp32), so 4 rows apart
             uint4 ca[NCQ], cb[NCQ];
 #pragma unroll
             for (int ch = 0; ch < NCQ; ++ch) {
-                ca[ch] = cp0[ch];
-                cb[ch] = cp1[ch];
+                ca[ch] = *reinterpret_cast<const uint4*>(ct + qoff[ch]);
+                cb[ch] = *reinterpret_cast<const uint4*>(ct + qoff[ch] + 4 * CSTR);
             }
             // every fragment read is in flight before the first product
             __builtin_amdgcn_sched_barrier(0);
@@ -306,14 +354,12 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             // group, lane r addresses row (slot) s0 + r/4 at dims d0 + 4*(r%4)
             // .. +3, and lane i receives slots s0..s0+3 of dim d0 + i; two
             // loads (s0 = 8g, 8g+4) give the lane's 8-slot fragment
-            const int rr = l & 15;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const int d0 = half * DVW + 16 * db;
-                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4s*)(ct + crow(8 * g + (rr >> 2)) + (d0 + 4 * (rr & 3)) * 2));
-                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4s*)(ct + crow(8 * g + 4 + (rr >> 2)) + (d0 + 4 * (rr & 3)) * 2));
+                // blocks 8 apart are 16 chunks apart: same XOR, +256 bytes
+                const unsigned char* tp = ct + poff[db & 7] + 256 * (db >> 3);
+                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)tp);
+                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tp + 4 * CSTR));
                 const uint2 a = __builtin_bit_cast(uint2, lo), b2 = __builtin_bit_cast(uint2, hi);
                 vb[db][0] = make_uint4(a.x, a.y, b2.x, b2.y);
             }
