@@ -322,8 +322,8 @@ TRAFFIC_SOURCES = ("indexer.hip", "tlsl_device.h", "tlsl_internal.h", "topk_comm
 TRAFFIC = {
     # profiles/prefill_score_kernel_bf16_n8192.md
     "prefill_score_kernel": {
-        "sources_sha256": "c7617df54d24104bacbd647582c90ba9ac47b89a157cd5ea582daca0a30d3ad4",
-        "fetch_kib": 85483.1719, "write_kib": 158355.9453,
+        "sources_sha256": "5c84ea8b9f1c726836e4bfc22a4a0a28e26f53b3fbad609ccf71a2390d989a10",
+        "fetch_kib": 85477.2812, "write_kib": 158355.2891,
         "copy_fetch_kib": 524313.5357, "copy_write_kib": 1048576.0, "copy_bytes": 1 << 30,
     },
 }
@@ -360,7 +360,7 @@ def main():
     ap.add_argument("--no-calib", action="store_true", help="skip the copy and matrix-core calibration")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (every workload runs on one "
+        print("bench.py measures one GPU: the library has no multi-GPU path (every workload runs on one "
               "device); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
