@@ -146,8 +146,9 @@ int topk_select(const float* scores, const int64_t* row_start, const int32_t* ro
  *   out [B,n,H,Dv] dtype dt,   lse [B,n,H] fp32 (optional)
  * Supported: dt=BF16 with (Dqk,Dv) = (576,512) (the 512-dim latent plus the
  * 64-dim position part) and 1 <= H <= 128; dt=F32 with (Dqk,Dv) = (80,64) and
- * 1 <= H <= 16.  Products and softmax run in fp32 (bf16 probabilities feed
- * the value product); softmax_scale must be positive and finite.
+ * 1 <= H <= 16; 1 <= k <= 4096 (larger k: TLSL_ERR_UNSUPPORTED).  Products
+ * and softmax run in fp32 (bf16 probabilities feed the value product);
+ * softmax_scale must be positive and finite.
  */
 int sparse_attn_prefill(const void* q, const void* kv, const int32_t* S, int B, int n, int H,
                         int Dqk, int Dv, int k, float softmax_scale, tlsl_dtype dt, void* out,

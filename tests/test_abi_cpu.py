@@ -158,6 +158,7 @@ def test_attention_validation():
     assert call(dt=2) == ERR_UNSUP
     assert call(Dqk=512) == ERR_UNSUP
     assert call(H=129) == ERR_UNSUP
+    assert call(k=4097) == ERR_UNSUP                                # one workgroup stages at most 4096 slots
     assert call(sc=0.0) == ERR_SHAPE
     assert call(sc=float("nan")) == ERR_SHAPE
     assert call(out=MIS) == ERR_ALIGN
@@ -168,6 +169,7 @@ def test_attention_validation():
     assert g(P, P, P, P, 64, 128, 576, 512, 2048, 0.04, 1, P, None, P,
              ctypes.byref(ctypes.c_size_t(size.value - 1)), None) == ERR_WS
     assert g(P, P, None, P, 64, 128, 576, 512, 2048, 0.04, 1, P, None, None, ctypes.byref(size), None) == ERR_NULL
+    assert g(P, P, P, P, 64, 128, 576, 512, 4097, 0.04, 1, P, None, None, ctypes.byref(size), None) == ERR_UNSUP
 
 
 def test_binding_refuses_when_library_missing(monkeypatch, tmp_path):

@@ -151,6 +151,7 @@ int sparse_attn_prefill(const void* q, const void* kv, const int32_t* S, int B, 
     if (!q || !kv || !S || !out) return fail(TLSL_ERR_NULL, "sparse_attn_prefill: NULL pointer argument");
     if (B <= 0 || n <= 0 || k <= 0 || H <= 0) return fail(TLSL_ERR_SHAPE, "sparse_attn_prefill: B, n, H and k must be positive");
     if ((int64_t)B * n > (int64_t)1 << 30) return fail(TLSL_ERR_SHAPE, "sparse_attn_prefill: B*n too large");
+    if (k > 4096) return fail(TLSL_ERR_UNSUPPORTED, "sparse_attn_prefill: k=%d above the supported 4096", k);
     if (dt != TLSL_F32 && dt != TLSL_BF16) return fail(TLSL_ERR_UNSUPPORTED, "sparse_attn_prefill: dtype %d not supported", dt);
     tlsl::AttnShape s{dt, H, Dqk, Dv};
     if (!tlsl::attn_supported(s))
@@ -171,6 +172,7 @@ int sparse_attn_decode(const void* q, const void* kv_cache, const int64_t* cu_se
                        void* workspace, size_t* ws_bytes, hipStream_t stream) {
     if (!q || !kv_cache || !cu_seqlens || !S || !out) return fail(TLSL_ERR_NULL, "sparse_attn_decode: NULL pointer argument");
     if (B <= 0 || k <= 0 || H <= 0) return fail(TLSL_ERR_SHAPE, "sparse_attn_decode: B, H and k must be positive");
+    if (k > 4096) return fail(TLSL_ERR_UNSUPPORTED, "sparse_attn_decode: k=%d above the supported 4096", k);
     if (dt != TLSL_F32 && dt != TLSL_BF16) return fail(TLSL_ERR_UNSUPPORTED, "sparse_attn_decode: dtype %d not supported", dt);
     tlsl::AttnShape s{dt, H, Dqk, Dv};
     if (!tlsl::attn_supported(s))
