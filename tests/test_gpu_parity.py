@@ -244,6 +244,29 @@ def test_sparse_attn_prefill(dt, H, Dqk, Dv, n, k):
     np.testing.assert_allclose(lse.cpu().numpy()[0][rows], ref_lse, rtol=1e-4, atol=1e-4)
 
 
+def test_sparse_attn_prefill_tile_pipeline():
+    # many tiles per row (every rotation of the tile buffers), whole tiles
+    # without a valid slot in the middle of a row, a ragged last tile (k=300)
+    # and a partial second head group (H=100)
+    n, H, k = 700, 100, 300
+    q, kv = synth.attn_prefill(1, n, H, 576, BF16, seed=14)
+    S = _random_selection(n, k, seed=7, messy=True)
+    S[::3, 32:96] = -1
+    S[1::5, 200:264] = -1
+    S = S[None]
+    scale = 1.0 / math.sqrt(576)
+    announce("sparse_attn_prefill tile pipeline")
+    out, lse = tl.sparse_attn_prefill(to_dev(q), to_dev(kv), torch.from_numpy(S).to(DEV), scale, 512,
+                                      want_lse=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_rows(n, k, 20, seed=5), [0, 1, 31, 32, 33, 95, 96, 299, 300, 699]]))
+    ref, ref_lse = oracle.sparse_attn_prefill_rows(BF16, host(q), host(kv), S, scale, rows, 512)
+    got = out.float().cpu().numpy()[0][rows]
+    err = np.abs(got - ref).max()
+    assert err <= parity.ATTN_ATOL_BF16, err
+    np.testing.assert_allclose(lse.cpu().numpy()[0][rows], ref_lse, rtol=1e-4, atol=1e-4)
+
+
 def test_sparse_attn_prefill_empty_rows():
     n, H, k = 20, 16, 64
     q, kv = synth.attn_prefill(1, n, H, 576, BF16, seed=12)
