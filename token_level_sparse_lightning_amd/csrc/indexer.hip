@@ -649,7 +649,9 @@ __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned cha
     __shared__ int pre[DEC2_MAXB + 1];
     __shared__ int64_t sstart[DEC2_MAXB + 1];
     __shared__ int scratch[16];
-    const int tid = threadIdx.x, wv_id = tid >> 6, l = lane_id();
+    // (wave index as a scalar: the subtile loop is then uniform, and the
+    // compiler adds no wait for all loads at its head)
+    const int tid = threadIdx.x, wv_id = __builtin_amdgcn_readfirstlane(tid >> 6), l = lane_id();
     // subtile prefix over the sequences, and the sequence starts
     int carry = 0;
     for (int b0 = 0; b0 < B; b0 += DEC2_NT) {
@@ -677,8 +679,14 @@ __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned cha
     uint4 qf[HB][NCH];
     float wv[HB][4];
     uint4 kf[2][4][NCH];
+    float ksc[2];
     // the wave's subtiles are g0+wv_id, +NWV, ...; they are walked one sequence
-    // (segment) at a time so that the inner loop has straight-line loads
+    // (segment) at a time so that the inner loop has straight-line loads.  A
+    // subtile's keys and key scales are loaded one step before its scores:
+    // both are loop-carried, so the compiler cannot sink the scale load next
+    // to the score store (where its wait would also wait for the prefetch).
+    // Loads past the segment end are clamped to its last key (in bounds,
+    // unused).
     int g = g0 + wv_id;
     while (g < g1) {
         const int b = find_seq(pre, B, g);
@@ -689,36 +697,22 @@ __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned cha
         const float wmul = (DT == kFP8) ? q_scale[b] : 1.f;
         I::load_query(q + (size_t)b * HI * I::ROWB, w + (size_t)b * HI, wmul, HI, true, qf, wv);
         int key0 = (g - pre[b]) * 64;
-        I::load_keys_global(kbase, key0, L - 1, kf[0]);
+        auto fetch = [&](int k0, uint4 (&kf_)[4][NCH], float& ks_) {
+            I::load_keys_global(kbase, min(k0, L - 1), L - 1, kf_);
+            ks_ = DT == kFP8 ? k_scale[start + min(k0 + l, L - 1)] : 1.f;
+        };
+        fetch(key0, kf[0], ksc[0]);
+        auto step = [&](const uint4 (&cur)[4][NCH], float ks, uint4 (&ahead)[4][NCH], float& ks_ahead) {
+            fetch(key0 + 64 * NWV, ahead, ks_ahead);
+            const float s = I::score_lean(qf, wv, cur) * ks;
+            if (key0 + l < L) scores[start + key0 + l] = s;
+            g += NWV;
+            key0 += 64 * NWV;
+            return g < seg_end;
+        };
         for (;;) {
-            // buffer 0 holds subtile g.  Issue this subtile's key scale first,
-            // then the next subtile's keys, so the scale arrives without
-            // waiting for the prefetch (loads complete in issue order).
-            float ks = 1.f;
-            if (DT == kFP8) ks = k_scale[start + min(key0 + l, L - 1)];
-            const int ga = g + NWV;
-            const int ka = key0 + 64 * NWV;
-            // unconditional (clamped, in bounds): a conditional load would force
-            // the compiler to wait for every outstanding load before using ks
-            I::load_keys_global(kbase, min(ka, L - 1), L - 1, kf[1]);
-            {
-                const float s = I::score_lean(qf, wv, kf[0]) * ks;
-                if (key0 + l < L) scores[start + key0 + l] = s;
-            }
-            g = ga;
-            key0 = ka;
-            if (g >= seg_end) break;
-            if (DT == kFP8) ks = k_scale[start + min(key0 + l, L - 1)];
-            const int gb = g + NWV;
-            const int kbk = key0 + 64 * NWV;
-            I::load_keys_global(kbase, min(kbk, L - 1), L - 1, kf[0]);
-            {
-                const float s = I::score_lean(qf, wv, kf[1]) * ks;
-                if (key0 + l < L) scores[start + key0 + l] = s;
-            }
-            g = gb;
-            key0 = kbk;
-            if (g >= seg_end) break;
+            if (!step(kf[0], ksc[0], kf[1], ksc[1])) break;
+            if (!step(kf[1], ksc[1], kf[0], ksc[0])) break;
         }
     }
 }
