@@ -322,8 +322,8 @@ TRAFFIC_SOURCES = ("indexer.hip", "tlsl_device.h", "tlsl_internal.h", "topk_comm
 TRAFFIC = {
     # profiles/prefill_score_kernel_bf16_n8192.md
     "prefill_score_kernel": {
-        "sources_sha256": "5c84ea8b9f1c726836e4bfc22a4a0a28e26f53b3fbad609ccf71a2390d989a10",
-        "fetch_kib": 85477.2812, "write_kib": 158355.2891,
+        "sources_sha256": "b51c24417f6b4fd80bf4fe0e2cc9d7ac5bfe5b2511c488eff7a5bf4874185e8e",
+        "fetch_kib": 85506.2969, "write_kib": 158356.3203,
         "copy_fetch_kib": 524313.5357, "copy_write_kib": 1048576.0, "copy_bytes": 1 << 30,
     },
 }
