@@ -10,9 +10,11 @@
 // the logits Z^T = C Q^T over the reduction dims (partial logits are exchanged
 // through LDS) and the output O^T = V^T P^T over the value dims -- so each wave
 // holds part of a query fragment and part of an output accumulator in
-// registers, leaving room to keep the next tile's rows in flight.  Per tile of
-// 32 slots the selected rows are gathered once into LDS, row-major
-// [slot][Dqk]: the A operand of Z^T is read from it directly and, for bf16,
+// registers.  Per tile of 32 slots the selected rows are gathered once into
+// LDS, row-major [slot][Dqk] (bf16: straight from global memory by the direct
+// global->LDS load, two tiles ahead, three rotating buffers, one barrier per
+// tile; fp32: through registers): the A operand of Z^T is read from it
+// directly and, for bf16,
 // the A operand of O^T (V^T) with the LDS transpose load; fp32 keeps a second,
 // transposed [Dv][slot] copy.  The slot order inside the first product is
 // permuted so that each lane's probabilities are exactly the P^T fragment the
@@ -34,6 +36,7 @@ constexpr int AT_KMAX = 4096;  // slots per workgroup (k <= 4096)
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) unsigned char lds_uc;
 
 // two floats to packed bf16 (round to nearest even; one gfx950 instruction)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -92,9 +95,9 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             return r * CSTR + (r >> 4) * 64 + 16 * k;
         }
     };
-    // bf16 (wave pairs): two tile buffers, the next tile is stored while this
-    // one is processed; fp32: one buffer
-    constexpr int NBUF = DSPLIT > 1 ? 2 : 1;
+    // bf16: three tile buffers, gathered straight into LDS two tiles ahead of
+    // the tile being computed; fp32: one buffer, stored from registers
+    constexpr int NBUF = EB == 2 ? 3 : 1;
     constexpr int CTB = AT_TS * CSTR + (EB == 2 ? 0 : (AT_TS / 16) * 64);  // bytes of one tile buffer
     __shared__ __align__(16) unsigned char ctile[NBUF][CTB];
     // fp32 values are also kept transposed ([d][slot]) for the P.V product;
@@ -104,11 +107,15 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     __shared__ int tile_any[AT_KMAX / AT_TS];
     __shared__ int tlist[AT_KMAX / AT_TS];
     __shared__ int ntl_sh;
-    // partial logits of each wave, lane-contiguous (conflict-free exchange)
-    __shared__ __align__(16) float4 zx0[DSPLIT > 1 ? NT : 1];
-    __shared__ __align__(16) float4 zx1[DSPLIT > 1 ? NT : 1];
+    // partial logits of each wave, lane-contiguous (conflict-free exchange);
+    // bf16: one set per tile parity (one barrier per tile separates a set's
+    // reads from its next writes only two tiles later)
+    constexpr int NZX = EB == 2 ? 2 : 1;
+    __shared__ __align__(16) float4 zx0[NZX][DSPLIT > 1 ? NT : 1];
+    __shared__ __align__(16) float4 zx1[NZX][DSPLIT > 1 ? NT : 1];
 
-    const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), g = l >> 4, c = l & 15;
+    const int tid = threadIdx.x, l = lane_id(), g = l >> 4, c = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hb = w / DSPLIT, half = w % DSPLIT;
     // workgroup -> (row, head group); two head groups of a row sit 8 apart
     const int HG = (a.H + HPW - 1) / HPW;
@@ -173,6 +180,9 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
                                                           (kd0 + g * (QKD / 4)) * EB);
 #pragma unroll
         for (int ch = 0; ch < NCQ; ++ch) qf[ch] = hvalid ? src[ch] : make_uint4(0, 0, 0, 0);
+        // wait here, once: otherwise the compiler places this wait (vmcnt(0))
+        // inside the tile loop, where it would also wait for the bf16 gather
+        __builtin_amdgcn_s_waitcnt(0xF70);
     }
     v4f o[NDB];
 #pragma unroll
@@ -181,8 +191,9 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     __syncthreads();
     const int ntl = ntl_sh;
 
-    // ---- gather of one tile: value part (quad of slots x 16-byte chunk) and
-    // position part (row x chunk); registers first, LDS after the compute ----
+    // ---- fp32 gather of one tile: value part (quad of slots x 16-byte chunk)
+    // and position part (row x chunk); registers first, LDS after the compute
+    // (bf16 gathers straight into LDS, below) ----
     constexpr int VITEMS = (AT_TS / 4) * (DV / VPC);
     constexpr int VPER = (VITEMS + NT - 1) / NT;
     constexpr int RC = (DQK - DV) / VPC;  // position-part chunks per row
@@ -200,18 +211,10 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     int vqd[VPER], rrow[RPER > 0 ? RPER : 1];
     const unsigned char* vsrc[VPER];
     const unsigned char* rsrc[RPER > 0 ? RPER : 1];
-    // value item -> (slot quad, chunk).  bf16: within 16 lanes, 4 consecutive
-    // chunks x 4 quads whose rows differ in f (conflict-free stores; 64-byte
-    // runs per entry in the gather); fp32: the quad varies fastest
+    // value item -> (slot quad, chunk), the quad varying fastest
     auto vitem = [](int it, int& qd, int& oc) {
-        if constexpr (EB == 2) {
-            static_assert(VITEMS == 512, "bf16 value items");
-            qd = (((it >> 2) & 3) << 1) | ((it >> 4) & 1);
-            oc = ((it >> 5) << 2) | (it & 3);
-        } else {
-            qd = it % (AT_TS / 4);
-            oc = it / (AT_TS / 4);
-        }
+        qd = it % (AT_TS / 4);
+        oc = it / (AT_TS / 4);
     };
 #pragma unroll
     for (int j = 0; j < VPER; ++j) {
@@ -304,12 +307,11 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
         }
     };
 
-    // the tile being computed sits in LDS while the next one is in flight into
-    // registers (loads are unconditional -- past the end they repeat the last
-    // tile -- so the compiler's wait counts stay exact)
-    // `mid` runs inside the tile's compute, after the P.V fragments are read
-    // and before the P.V products (the next tile's LDS store goes there)
-    auto compute = [&](int tcur, const unsigned char* ct, auto&& mid) {
+    // one tile: logits, exchange, softmax, P.V.  `mid` runs after the P.V
+    // fragments are read and before the P.V products; `pre` and `post` run
+    // just before and just after the barrier of the logit exchange (bf16: the
+    // gather's wait and its next issue)
+    auto compute = [&](int tcur, const unsigned char* ct, int par, auto&& pre, auto&& post, auto&& mid) {
         const int* sl = slots + tcur * AT_TS;
 
         // ---- logits: Z^T[slot][head]; lane (g,c) gets slots 8g..8g+7 of head c
@@ -333,10 +335,12 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             }
             if constexpr (DSPLIT > 1) {
                 // add the partner wave's partial logits (the same sum in both waves)
-                zx0[tid] = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
-                zx1[tid] = make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
+                zx0[par][tid] = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
+                zx1[par][tid] = make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
+                pre();
                 __syncthreads();
-                const float4 o0 = zx0[tid ^ 64], o1 = zx1[tid ^ 64];
+                post();
+                const float4 o0 = zx0[par][tid ^ 64], o1 = zx1[par][tid ^ 64];
                 acc0[0] += o0.x; acc0[1] += o0.y; acc0[2] += o0.z; acc0[3] += o0.w;
                 acc1[0] += o1.x; acc1[1] += o1.y; acc1[2] += o1.z; acc1[3] += o1.w;
             }
@@ -427,57 +431,86 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
         for (int ti = 0; ti < ntl; ++ti) {
             load_tile(tlist[min(ti + 1, ntl - 1)], P);
             asm volatile("" ::: "memory");
-            compute(tlist[ti], ctile[0], none);
+            compute(tlist[ti], ctile[0], 0, none, none, none);
             __syncthreads();
             if (ti + 1 >= ntl) break;
             store_tile(P, ctile[0]);
-            __syncthreads();
-        }
-    } else if constexpr (!DECODE) {
-        // prefill (rows mostly cache-resident): one tile ahead in registers;
-        // it is stored into the idle buffer during this tile's compute (every
-        // read of that buffer ended before the last barrier)
-        Pre P;
-        if (ntl > 0) {
-            load_tile(tlist[0], P);
-            store_tile(P, ctile[0]);
-        }
-        __syncthreads();
-        for (int ti = 0; ti < ntl; ++ti) {
-            const bool more = ti + 1 < ntl;
-            load_tile(tlist[min(ti + 1, ntl - 1)], P);
-            asm volatile("" ::: "memory");
-            compute(tlist[ti], ctile[ti & 1], [&] {
-                asm volatile("" ::: "memory");
-                if (more) store_tile(P, ctile[(ti + 1) & 1]);
-            });
             __syncthreads();
         }
     } else {
-        // decode (cold rows from a large cache): two tiles ahead in registers
-        Pre P0, P1;
-        if (ntl > 0) {
-            load_tile(tlist[0], P0);
-            store_tile(P0, ctile[0]);
-            load_tile(tlist[min(1, ntl - 1)], P0);
+        // bf16: the tile's 36 KB go from global memory into LDS by the direct
+        // global->LDS load, 1 KB (64 lanes x 16 bytes) per instruction, M0 the
+        // block's LDS address; wave w loads blocks w, w+8, ... < 36.  Lane l
+        // of block b fills tile byte 1024b + 16l, i.e. row r = (64b + l)/72,
+        // stored chunk (64b + l) % 72, whose source is the entry's chunk
+        // under the inverse swizzle (the XOR is its own inverse).  The loads
+        // are inline asm: the compiler neither waits for them before
+        // unrelated LDS reads nor counts them; the waits below (vmcnt, then
+        // the exchange barrier) make a tile visible before any wave reads it.
+        // Tile k sits in buffer k % 3; tile k+2 is issued right after the
+        // barrier of tile k, into the buffer tile k-1 left (whose last reads,
+        // the transpose loads of tile k-1, preceded that barrier), and has
+        // landed by the barrier of tile k+1.  An invalid slot reads entry 0 of
+        // the row's sequence (in bounds); its logit is masked to -inf.
+        constexpr int NBLK = AT_TS * CROW / 1024;  // 36
+        const int nblk = (NBLK - w + 7) / 8;       // 5 or 4
+        int drow[5], doff[5];
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const int p = min(64 * (w + 8 * i) + l, AT_TS * (CROW / 16) - 1);
+            const int r = p / (CROW / 16), kk = p % (CROW / 16);
+            const int f = ((r >> 3) << 2) | (r & 3);
+            drow[i] = r;
+            doff[i] = 16 * (kk < 64 ? ((kk & ~15) | ((kk ^ f) & 15)) : (64 | ((kk ^ (f >> 1)) & 7)));
         }
-        __syncthreads();
-        for (int ti = 0; ti < ntl; ti += 2) {
-            load_tile(tlist[min(ti + 2, ntl - 1)], P1);
-            asm volatile("" ::: "memory");
-            compute(tlist[ti], ctile[0], [&] {
-                asm volatile("" ::: "memory");
-                if (ti + 1 < ntl) store_tile(P0, ctile[1]);
-            });
+        const uint32_t ct_lds = (uint32_t)(uintptr_t)(lds_uc*)&ctile[0][0];
+        int dpos[5];
+        auto fetch_pos = [&](int t) {
+            const int* sl = slots + t * AT_TS;
+#pragma unroll
+            for (int i = 0; i < 5; ++i) dpos[i] = max(sl[drow[i]], 0);
+        };
+        auto issue_dma = [&](int buf) {
+            const uint32_t B = ct_lds + buf * CTB;
+#pragma unroll
+            for (int i = 0; i < 5; ++i) {
+                if (i == 4 && nblk < 5) break;
+                const uint64_t a64 = (uint64_t)(uintptr_t)(kvrow + (size_t)dpos[i] * CROW + doff[i]);
+                const uint32_t m0v = B + 1024 * (w + 8 * i);
+                asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                             :
+                             : "s"(m0v), "v"(a64)
+                             : "memory");
+            }
+        };
+        if (ntl > 0) {
+            fetch_pos(tlist[0]);
+            issue_dma(0);
+            if (ntl > 1) {
+                fetch_pos(tlist[1]);
+                issue_dma(1);
+                // tile 0 landed; tile 1 (this wave's last 5 or 4 loads) may be in flight
+                if (nblk == 5)
+                    __builtin_amdgcn_s_waitcnt(0xF75);  // vmcnt(5)
+                else
+                    __builtin_amdgcn_s_waitcnt(0xF74);  // vmcnt(4)
+            } else {
+                __builtin_amdgcn_s_waitcnt(0xF70);      // vmcnt(0)
+            }
             __syncthreads();
-            if (ti + 1 >= ntl) break;
-            load_tile(tlist[min(ti + 3, ntl - 1)], P0);
-            asm volatile("" ::: "memory");
-            compute(tlist[ti + 1], ctile[1], [&] {
-                asm volatile("" ::: "memory");
-                if (ti + 2 < ntl) store_tile(P1, ctile[0]);
-            });
-            __syncthreads();
+            int cur = 0, nxt = 2;
+            for (int ti = 0; ti < ntl; ++ti) {
+                const bool more = ti + 2 < ntl;
+                if (more) fetch_pos(tlist[ti + 2]);
+                compute(tlist[ti], ctile[cur], ti & 1,
+                        [&] { __builtin_amdgcn_s_waitcnt(0xF70); },  // vmcnt(0): tile ti+1 landed
+                        [&] {
+                            if (more) issue_dma(nxt);
+                        },
+                        none);
+                cur = cur == 2 ? 0 : cur + 1;
+                nxt = nxt == 2 ? 0 : nxt + 1;
+            }
         }
     }
 
