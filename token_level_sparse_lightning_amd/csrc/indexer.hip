@@ -459,8 +459,10 @@ struct FinalizeArgs {
 
 template <int CAPMAX>
 __global__ __launch_bounds__(FIN_NT) void prefill_finalize_kernel(FinalizeArgs a) {
-    __shared__ uint32_t fkey[CAPMAX];  // order-preserving keys, ascending position
-    __shared__ int fpos[CAPMAX];
+    // order-preserving keys in ascending position order; the positions are
+    // read back from the candidate buffer (L2-resident) when the selection is
+    // written, so that four workgroups fit per CU
+    __shared__ uint32_t fkey[CAPMAX];
     __shared__ SelectSmem sel;
     const int tid = threadIdx.x;
     const int row = blockIdx.x;
@@ -473,9 +475,8 @@ __global__ __launch_bounds__(FIN_NT) void prefill_finalize_kernel(FinalizeArgs a
     }
     const uint2* src = a.buf + (size_t)row * a.cap;
     if (cnt > 0)
-        batched_copy<FIN_NT, 16>(cnt, [&](int i) { return src[i]; }, [&](int i, uint2 e) {
+        batched_copy<FIN_NT, 8>(cnt, [&](int i) { return src[i]; }, [&](int i, uint2 e) {
             fkey[cnt - 1 - i] = score_key(__uint_as_float(e.x));  // the buffer holds descending positions
-            fpos[cnt - 1 - i] = (int)e.y;
         });
     __syncthreads();
     uint32_t T = 0u;  // key of the K-th largest candidate
@@ -490,6 +491,12 @@ __global__ __launch_bounds__(FIN_NT) void prefill_finalize_kernel(FinalizeArgs a
     // with the K-th key are taken in position order until K are selected.
     const int seg = (cnt + FIN_NT - 1) / FIN_NT;
     const int b0 = min(tid * seg, cnt), b1 = min(b0 + seg, cnt);
+    // this thread's positions, loaded unconditionally (clamped) so that they
+    // are all in flight during the counting and the scan
+    constexpr int SEGMAX = (CAPMAX + FIN_NT - 1) / FIN_NT;
+    int mypos[SEGMAX];
+#pragma unroll
+    for (int u = 0; u < SEGMAX; ++u) mypos[u] = (int)src[max(cnt - 1 - min(b0 + u, cnt - 1), 0)].y;
     int ngt = 0, ntie = 0;
     for (int i = b0; i < b1; ++i) {
         const uint32_t key = fkey[i];
@@ -500,12 +507,15 @@ __global__ __launch_bounds__(FIN_NT) void prefill_finalize_kernel(FinalizeArgs a
     block_scan_int2<FIN_NT>(ngt, ntie, &egt, &etie, &tgt, &ttie, sel.scratch);
     int slot = egt + min(etie, need_ties);
     int ties_before = etie;
-    for (int i = b0; i < b1; ++i) {
+#pragma unroll
+    for (int u = 0; u < SEGMAX; ++u) {
+        const int i = b0 + u;
+        if (i >= b1) break;
         const uint32_t key = fkey[i];
         bool sel = key > T;
         if (key == T) sel = ties_before++ < need_ties;
         if (sel) {
-            Srow[slot] = fpos[i];
+            Srow[slot] = mypos[u];
             if (Ssrow) Ssrow[slot] = key_score(key);
             ++slot;
         }
