@@ -322,8 +322,8 @@ TRAFFIC_SOURCES = ("indexer.hip", "tlsl_device.h", "tlsl_internal.h", "topk_comm
 TRAFFIC = {
     # profiles/prefill_score_kernel_bf16_n8192.md
     "prefill_score_kernel": {
-        "sources_sha256": "b51c24417f6b4fd80bf4fe0e2cc9d7ac5bfe5b2511c488eff7a5bf4874185e8e",
-        "fetch_kib": 85506.2969, "write_kib": 158356.3203,
+        "sources_sha256": "dc6ecec084966f6eff9af5a12c1dedd67bdcd20822b2ed3ecda590ff5fb2f1ed",
+        "fetch_kib": 85515.1562, "write_kib": 158356.2969,
         "copy_fetch_kib": 524313.5357, "copy_write_kib": 1048576.0, "copy_bytes": 1 << 30,
     },
 }
