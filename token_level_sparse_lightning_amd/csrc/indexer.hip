@@ -65,41 +65,60 @@ struct Idx {
         }
     }
 
+    // Products of one query's head blocks with key block kb (accumulators
+    // start at zero; the HB head blocks are independent accumulation chains,
+    // interleaved step by step).
+    __device__ __forceinline__ static void products(const uint4 (&qf)[HB][NCH], const uint4 (&kfb)[NCH],
+                                                    v4f (&A)[HB]) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) A[hb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < M::STEPS; ++st)
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) A[hb] = M::step(qf[hb], kfb, st, A[hb]);
+    }
+    // ReLU, head weights and the lane's part of the head sum of one key block.
+    __device__ __forceinline__ static float epilogue(const float (&wv)[HB][4], const v4f (&A)[HB]) {
+        float p = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p = __builtin_fmaf(wv[hb][r], relu(A[hb][r]), p);
+        return p;
+    }
+
     // Scores of one query against a 64-key subtile whose key fragments are
-    // kf[kb] (keys 16*kb + (l & 15)).  Lane l receives key l's score (before
-    // the key scale).
+    // kf[kb] (keys 16*kb + (l & 15)), in two parts: score_head() runs the
+    // products of the four key blocks and the epilogues of the first three
+    // (accumulators alternate between two sets, so the epilogue of key block
+    // kb runs while the products of kb+1 are in flight) and leaves the last
+    // block's products in `last`; score_tail() finishes.  score() is the two
+    // back to back.  Lane l receives key l's score (before the key scale); the
+    // operations and their order are fixed, so every caller gets bit-identical
+    // scores.
+    __device__ __forceinline__ static void score_head(const uint4 (&qf)[HB][NCH], const float (&wv)[HB][4],
+                                                      const uint4 (&kf)[4][NCH], float (&part)[3],
+                                                      v4f (&last)[HB]) {
+        v4f acc[HB];
+        products(qf, kf[0], acc);
+        products(qf, kf[1], last);
+        part[0] = epilogue(wv, acc);
+        products(qf, kf[2], acc);
+        part[1] = epilogue(wv, last);
+        products(qf, kf[3], last);
+        part[2] = epilogue(wv, acc);
+    }
+    __device__ __forceinline__ static float score_tail(const float (&wv)[HB][4], const float (&part)[3],
+                                                       const v4f (&last)[HB]) {
+        const float p[4] = {part[0], part[1], part[2], epilogue(wv, last)};
+        return reduce_heads_64(p);
+    }
     __device__ __forceinline__ static float score(const uint4 (&qf)[HB][NCH], const float (&wv)[HB][4],
                                                   const uint4 (&kf)[4][NCH]) {
-        // the HB head blocks are independent accumulation chains, interleaved
-        // step by step; accumulators alternate between two sets so that the
-        // epilogue of key block kb runs while the products of kb+1 are in flight
-        v4f acc[2][HB];
-        auto products = [&](int kb, v4f (&A)[HB]) {
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) A[hb] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int st = 0; st < M::STEPS; ++st)
-#pragma unroll
-                for (int hb = 0; hb < HB; ++hb) A[hb] = M::step(qf[hb], kf[kb], st, A[hb]);
-        };
-        auto epilogue = [&](const v4f (&A)[HB]) {
-            float p = 0.f;
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) p = __builtin_fmaf(wv[hb][r], relu(A[hb][r]), p);
-            return p;
-        };
-        float part[4];
-        products(0, acc[0]);
-        products(1, acc[1]);
-        part[0] = epilogue(acc[0]);
-        products(2, acc[0]);
-        part[1] = epilogue(acc[1]);
-        products(3, acc[1]);
-        part[2] = epilogue(acc[0]);
-        part[3] = epilogue(acc[1]);
-        return reduce_heads_64(part);
+        float part[3];
+        v4f last[HB];
+        score_head(qf, wv, kf, part, last);
+        return score_tail(wv, part, last);
     }
 
     // The same scores with one accumulator set (fewer registers, more waves
@@ -369,9 +388,29 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
     }
 
     // ---- main pass: every causal key, diagonal first -----------------------
+    // The last query of each subtile is finished one iteration late: its final
+    // epilogue, head sum, threshold test and append run after the next
+    // barrier, once the next subtile's fragment loads are issued, so that this
+    // dependent tail overlaps the LDS latency instead of idling the matrix
+    // cores before the barrier.  Appends stay in descending position order.
     int cntq[QW];
 #pragma unroll
     for (int i = 0; i < QW; ++i) cntq[i] = 0;
+    // threshold test and ordered append slot of query i's scores sc at positions s
+    auto select = [&](int i, float sc, int s, bool& st, size_t& idx, uint2& val) {
+        const bool ok = s <= tq[i] && sc >= theta[i];
+        const uint64_t m = ballot(ok);
+        const int slot = cntq[i] + rank_above(m);
+        st = ok && slot < a.cap;
+        idx = (tok0 + tq[i]) * (size_t)a.cap + slot;
+        val = make_uint2(__float_as_uint(sc), (uint32_t)s);
+        cntq[i] += __popcll(m);
+    };
+    float tpart[3];
+    v4f tlast[HB];
+    float tks = 1.f;
+    int ts = 0;
+    bool tpend = false;
     const int nsub = t_last / 64 + 1;
     __syncthreads();
     copy_rows(ktile[0], (nsub - 1) * 64, 1);
@@ -394,11 +433,22 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
         asm volatile("" ::: "memory");
         uint4 kf[4][NCH];
         frag_from_lds(ktile[cur], kf);
-        const int s = j * 64 + l;
-        const float ks = (DT == kFP8) ? a.k_scale[tok0 + min(s, a.n - 1)] : 1.f;
+        // the fragment loads stay ahead of the previous subtile's tail
+        __builtin_amdgcn_sched_barrier(0);
         // candidate appends are held until the prefetched subtile is in LDS:
         // a store issued between the prefetch loads and their use would make
         // the wait for the loads wait for the store as well
+        bool tst = false;
+        size_t tidx = 0;
+        uint2 tval = make_uint2(0, 0);
+        if (tpend) {
+            float sc = I::score_tail(wv[QW - 1], tpart, tlast);
+            if (DT == kFP8) sc *= tks;
+            select(QW - 1, sc, ts, tst, tidx, tval);
+        }
+        tpend = false;
+        const int s = j * 64 + l;
+        const float ks = (DT == kFP8) ? a.k_scale[tok0 + min(s, a.n - 1)] : 1.f;
         bool cst[QW];
         size_t cidx[QW];
         uint2 cval[QW];
@@ -406,15 +456,16 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
         for (int i = 0; i < QW; ++i) {
             cst[i] = false;
             if (!qv[i] || j * 64 > tq[i]) continue;
-            float sc = I::score(qf[i], wv[i], kf);
-            if (DT == kFP8) sc *= ks;
-            const bool ok = s <= tq[i] && sc >= theta[i];
-            const uint64_t m = ballot(ok);
-            const int slot = cntq[i] + rank_above(m);
-            cst[i] = ok && slot < a.cap;
-            cidx[i] = (tok0 + tq[i]) * (size_t)a.cap + slot;
-            cval[i] = make_uint2(__float_as_uint(sc), (uint32_t)s);
-            cntq[i] += __popcll(m);
+            if (i < QW - 1) {
+                float sc = I::score(qf[i], wv[i], kf);
+                if (DT == kFP8) sc *= ks;
+                select(i, sc, s, cst[i], cidx[i], cval[i]);
+            } else {
+                I::score_head(qf[i], wv[i], kf, tpart, tlast);
+                ts = s;
+                tks = ks;
+                tpend = true;
+            }
         }
         asm volatile("" ::: "memory");
         {
@@ -430,10 +481,20 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
             pf_store(0, pre0);
             if (PER > 1) pf_store(1, pre1);
         }
+        if (tst) a.buf[tidx] = tval;
 #pragma unroll
         for (int i = 0; i < QW; ++i)
             if (cst[i]) a.buf[cidx[i]] = cval[i];
         __syncthreads();
+    }
+    if (tpend) {
+        bool tst;
+        size_t tidx;
+        uint2 tval;
+        float sc = I::score_tail(wv[QW - 1], tpart, tlast);
+        if (DT == kFP8) sc *= tks;
+        select(QW - 1, sc, ts, tst, tidx, tval);
+        if (tst) a.buf[tidx] = tval;
     }
     if (l == 0) {
 #pragma unroll
@@ -784,14 +845,13 @@ PrefillPlan plan_prefill(const IndexerShape& s, int B, int n, int k) {
 template <int DT, int HB, int DI>
 static hipError_t launch_prefill_t(const PrefillArgs& pa, const FinalizeArgs& fa, const FallbackArgs& fb,
                                    int qw, int rows, int cap, int fb_blocks, hipStream_t st) {
-    if (qw == 2)
-        TLSL_TIMED_LAUNCH("prefill_score_kernel", st,
-                          hipLaunchKernelGGL((prefill_score_kernel<DT, HB, DI, 2>), dim3(pa.tiles * pa.B), dim3(PF_NT), 0,
-                                             st, pa));
-    else
-        TLSL_TIMED_LAUNCH("prefill_score_kernel", st,
-                          hipLaunchKernelGGL((prefill_score_kernel<DT, HB, DI, 1>), dim3(pa.tiles * pa.B), dim3(PF_NT), 0,
-                                             st, pa));
+    // two queries per wave only where the fragments of both fit in registers
+    // (the rule of queries_per_wave); the other form is not instantiated
+    constexpr int QW = Mma<DT, DI>::NCH * HB <= 8 ? 2 : 1;
+    if (qw != QW) return hipErrorInvalidValue;
+    TLSL_TIMED_LAUNCH("prefill_score_kernel", st,
+                      hipLaunchKernelGGL((prefill_score_kernel<DT, HB, DI, QW>), dim3(pa.tiles * pa.B), dim3(PF_NT), 0,
+                                         st, pa));
     if (cap <= 1024)
         TLSL_TIMED_LAUNCH("prefill_finalize_kernel", st,
                           hipLaunchKernelGGL((prefill_finalize_kernel<1024>), dim3(rows), dim3(FIN_NT), 0, st, fa));
