@@ -18,7 +18,8 @@
 //     buffer (radix select in LDS) and writes S in ascending position order.
 //     A row whose buffer missed (fewer candidates than min(k, t+1): the sample
 //     threshold overshot) or overflowed goes on a fallback list.
-//  3. prefill_fallback: rescores each listed row in full and selects from it.
+//  3. prefill_fallback: rescores the listed rows in full (spread over the
+//     whole grid) and selects from them.
 // The result does not depend on the threshold: every key that can be in the
 // top-k reaches the buffer, or the row is recomputed.
 //
@@ -601,36 +602,70 @@ struct FallbackArgs {
     int n, HI, topk;
     const int* fb_count;
     const int* fb_list;
-    float* scratch;  // [gridDim.x][n]
+    float* scratch;  // [fallback workgroups][n]
     int32_t* S;
     float* Ss;
 };
 
+// Scores of fallback row `row` for the 64-key subtiles j = j0, j0 + jstep, ...
+// below j1, into sc[0..t] (one wave per subtile; the same tile code as the
+// main pass, so the scores are bit-identical to it).
 template <int DT, int HB, int DI>
-__global__ __launch_bounds__(FB_NT) void prefill_fallback_kernel(FallbackArgs a) {
+__device__ __forceinline__ void fallback_rescore(const FallbackArgs& a, int row, int j0, int j1, int jstep,
+                                                 float* sc) {
     using I = Idx<DT, HB, DI>;
     constexpr int NCH = I::NCH;
+    const int l = lane_id();
+    const int t = row % a.n;
+    const size_t tok0 = (size_t)row - t;
+    uint4 qf[HB][NCH];
+    float wv[HB][4];
+    const float wmul = (DT == kFP8) ? a.q_scale[row] : 1.f;
+    I::load_query(a.q + (size_t)row * a.HI * I::ROWB, a.w + (size_t)row * a.HI, wmul, a.HI, true, qf, wv);
+    const unsigned char* kb_base = a.k + tok0 * I::ROWB;
+    for (int j = j0; j < j1 && j * 64 <= t; j += jstep) {
+        uint4 kf[4][NCH];
+        I::load_keys_global(kb_base, j * 64, t, kf);
+        float s = I::score(qf, wv, kf);
+        const int key = j * 64 + l;
+        if (DT == kFP8) s *= a.k_scale[tok0 + min(key, t)];
+        if (key <= t) sc[key] = s;
+    }
+}
+
+// Stage 3a: the first gridDim(3b) entries of the fallback list are rescored
+// in parallel: work items (entry i, chunk of FBS_CHUNK keys) spread over the
+// whole grid; entry i's scores go to scratch row i.  (A rare miss would
+// otherwise rescore a whole row on one compute unit.)
+constexpr int FBS_NT = 512;
+constexpr int FBS_CHUNK = 4096;
+constexpr int FBS_BLOCKS = 256;
+
+template <int DT, int HB, int DI>
+__global__ __launch_bounds__(FBS_NT) void prefill_fallback_score_kernel(FallbackArgs a, int fb_rows) {
+    const int nfb = min(*a.fb_count, fb_rows);
+    const int nch = (a.n + FBS_CHUNK - 1) / FBS_CHUNK;
+    const int w = threadIdx.x >> 6;
+    for (int item = blockIdx.x; item < nfb * nch; item += gridDim.x) {
+        const int i = item / nch, c = item - i * nch;
+        const int row = a.fb_list[i];
+        constexpr int SUB = FBS_CHUNK / 64;
+        fallback_rescore<DT, HB, DI>(a, row, c * SUB + w, (c + 1) * SUB, FBS_NT / 64, a.scratch + (size_t)i * a.n);
+    }
+}
+
+// Stage 3b: each fallback row is selected from its full score row; entries
+// past the first gridDim.x (not rescored by stage 3a) are rescored here.
+template <int DT, int HB, int DI>
+__global__ __launch_bounds__(FB_NT) void prefill_fallback_kernel(FallbackArgs a) {
     __shared__ TopkSmem sm;
     const int nfb = *a.fb_count;
-    const int w = threadIdx.x >> 6, l = lane_id();
+    const int w = threadIdx.x >> 6;
     float* sc = a.scratch + (size_t)blockIdx.x * a.n;
     for (int it = blockIdx.x; it < nfb; it += gridDim.x) {
         const int row = a.fb_list[it];
         const int t = row % a.n;
-        const size_t tok0 = (size_t)row - t;
-        uint4 qf[HB][NCH];
-        float wv[HB][4];
-        const float wmul = (DT == kFP8) ? a.q_scale[row] : 1.f;
-        I::load_query(a.q + (size_t)row * a.HI * I::ROWB, a.w + (size_t)row * a.HI, wmul, a.HI, true, qf, wv);
-        const unsigned char* kb_base = a.k + tok0 * I::ROWB;
-        for (int j = w; j * 64 <= t; j += FB_NT / 64) {
-            uint4 kf[4][NCH];
-            I::load_keys_global(kb_base, j * 64, t, kf);
-            float s = I::score(qf, wv, kf);
-            const int key = j * 64 + l;
-            if (DT == kFP8) s *= a.k_scale[tok0 + min(key, t)];
-            if (key <= t) sc[key] = s;
-        }
+        if (it >= (int)gridDim.x) fallback_rescore<DT, HB, DI>(a, row, w, 1 << 30, FB_NT / 64, sc);
         __threadfence();
         __syncthreads();
         __threadfence();
@@ -823,7 +858,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 PrefillPlan plan_prefill(const IndexerShape& s, int B, int n, int k) {
     PrefillPlan p{};
     p.cap = (int)((2 * (size_t)k + 256 + 255) / 256 * 256);
-    p.stride = k >= 2048 ? 16 : (k >= 128 ? k / 128 : 1);
+    p.stride = std::max(1, k / 64);  // ~64 sample keys expected inside the top-k
     p.fb_blocks = 128;
     const size_t rows = (size_t)B * n;
     size_t off = 0;
@@ -861,6 +896,9 @@ static hipError_t launch_prefill_t(const PrefillArgs& pa, const FinalizeArgs& fa
     else
         TLSL_TIMED_LAUNCH("prefill_finalize_kernel", st,
                           hipLaunchKernelGGL((prefill_finalize_kernel<8448>), dim3(rows), dim3(FIN_NT), 0, st, fa));
+    TLSL_TIMED_LAUNCH("prefill_fallback_score_kernel", st,
+                      hipLaunchKernelGGL((prefill_fallback_score_kernel<DT, HB, DI>), dim3(FBS_BLOCKS), dim3(FBS_NT), 0,
+                                         st, fb, fb_blocks));
     TLSL_TIMED_LAUNCH("prefill_fallback_kernel", st,
                       hipLaunchKernelGGL((prefill_fallback_kernel<DT, HB, DI>), dim3(fb_blocks), dim3(FB_NT), 0, st, fb));
     return hipGetLastError();
