@@ -547,15 +547,21 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
 }
 
 // Merge the split partials of a decode row: o = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s.
-// One workgroup per (row, head); each thread owns DV/CB_NT consecutive dims.
-constexpr int CB_NT = 128;
+// One wave per (row, head), CB_NT/64 heads per workgroup; lane l owns value
+// dims [l*DV/64, (l+1)*DV/64) (16-byte loads and stores).
+constexpr int CB_NT = 256;
 
 template <int DT, int DV>
-__global__ __launch_bounds__(CB_NT) void attn_combine_kernel(const float* part_o, const float* part_ml, int H, int nsplit,
-                                                             unsigned char* out, float* lse) {
+__global__ __launch_bounds__(CB_NT) void attn_combine_kernel(const float* part_o, const float* part_ml, int rows, int H,
+                                                             int nsplit, unsigned char* out, float* lse) {
     constexpr int EB = ElemBytes<DT>::v;
-    constexpr int PER = (DV + CB_NT - 1) / CB_NT;
-    const int row = blockIdx.x / H, h = blockIdx.x % H;
+    constexpr int PER = DV / 64;
+    static_assert(DV % 64 == 0 && (PER < 4 || PER % 4 == 0), "whole dims (or float4 groups) per lane");
+    constexpr int VW = PER >= 4 ? 4 : 1;  // floats per load
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = lane_id();
+    const int rh = blockIdx.x * (CB_NT / 64) + wv;  // row * H + head
+    if (rh >= rows * H) return;
+    const int row = rh / H, h = rh - row * H;
     float M = -INFINITY;
     for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(((size_t)row * nsplit + s) * H + h) * 2]);
     float L = 0.f, acc[PER];
@@ -567,26 +573,37 @@ __global__ __launch_bounds__(CB_NT) void attn_combine_kernel(const float* part_o
             const float ms = part_ml[pidx * 2];
             const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
             L += f * part_ml[pidx * 2 + 1];
-            const float* po = part_o + pidx * DV;
+            const float* po = part_o + pidx * DV + l * PER;
 #pragma unroll
-            for (int j = 0; j < PER; ++j) {
-                const int d = threadIdx.x * PER + j;
-                if (d < DV) acc[j] += f * po[d];
+            for (int j = 0; j < PER; j += VW) {
+                if constexpr (VW == 4) {
+                    const float4 v = *reinterpret_cast<const float4*>(po + j);
+                    acc[j] += f * v.x;
+                    acc[j + 1] += f * v.y;
+                    acc[j + 2] += f * v.z;
+                    acc[j + 3] += f * v.w;
+                } else {
+                    acc[j] += f * po[j];
+                }
             }
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    const size_t ob = ((size_t)row * H + h) * DV;
+    unsigned char* op = out + (((size_t)row * H + h) * DV + l * PER) * EB;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int d = threadIdx.x * PER + j;
-        if (d >= DV) continue;
-        if constexpr (EB == 2)
-            reinterpret_cast<uint16_t*>(out)[ob + d] = f32_to_bf16_rne(acc[j] * inv);
+    for (int j = 0; j < PER; j += VW) {
+        if constexpr (VW == 4 && EB == 2)
+            *reinterpret_cast<uint2*>(op + 2 * j) = make_uint2(pack_bf16x2(acc[j] * inv, acc[j + 1] * inv),
+                                                               pack_bf16x2(acc[j + 2] * inv, acc[j + 3] * inv));
+        else if constexpr (VW == 4)
+            *reinterpret_cast<float4*>(op + 4 * j) =
+                make_float4(acc[j] * inv, acc[j + 1] * inv, acc[j + 2] * inv, acc[j + 3] * inv);
+        else if constexpr (EB == 2)
+            reinterpret_cast<uint16_t*>(op)[j] = f32_to_bf16_rne(acc[j] * inv);
         else
-            reinterpret_cast<float*>(out)[ob + d] = acc[j] * inv;
+            reinterpret_cast<float*>(op)[j] = acc[j] * inv;
     }
-    if (lse && threadIdx.x == 0) lse[(size_t)row * H + h] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+    if (lse && l == 0) lse[(size_t)row * H + h] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -675,14 +692,15 @@ hipError_t launch_sparse_attn_decode(const AttnShape& s, const void* q, const vo
     }
     dispatch_attn<true>(s, a, B * ns, st);
     if (ns > 1) {
+        const int grid = (B * s.H + CB_NT / 64 - 1) / (CB_NT / 64);
         if (s.dt == kBF16)
             TLSL_TIMED_LAUNCH("attn_combine_kernel", st,
-                              hipLaunchKernelGGL((attn_combine_kernel<kBF16, 512>), dim3(B * s.H), dim3(CB_NT), 0, st,
-                                                 a.part_o, a.part_ml, s.H, ns, a.out, lse));
+                              hipLaunchKernelGGL((attn_combine_kernel<kBF16, 512>), dim3(grid), dim3(CB_NT), 0, st,
+                                                 a.part_o, a.part_ml, B, s.H, ns, a.out, lse));
         else
             TLSL_TIMED_LAUNCH("attn_combine_kernel", st,
-                              hipLaunchKernelGGL((attn_combine_kernel<kF32, 64>), dim3(B * s.H), dim3(CB_NT), 0, st,
-                                                 a.part_o, a.part_ml, s.H, ns, a.out, lse));
+                              hipLaunchKernelGGL((attn_combine_kernel<kF32, 64>), dim3(grid), dim3(CB_NT), 0, st,
+                                                 a.part_o, a.part_ml, B, s.H, ns, a.out, lse));
     }
     return hipGetLastError();
 }
