@@ -29,6 +29,7 @@ a bounded sample of query rows of the headline workload.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -82,13 +83,20 @@ def time_calls(fn, steps, warmup, kernel=None):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     if kernel:
         tl.timer_arm(kernel, max_launches=8 * steps)
-    t0 = time.perf_counter()
-    for a, b in evs:
-        a.record(st)
-        fn()
-        b.record(st)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
+    # no garbage collection inside the timed region (a collection pass over
+    # the input generator's bookkeeping can take tens of milliseconds)
+    gc.collect()
+    gc.disable()
+    try:
+        t0 = time.perf_counter()
+        for a, b in evs:
+            a.record(st)
+            fn()
+            b.record(st)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+    finally:
+        gc.enable()
     kern = tl.timer_collect() if kernel else None
     return Timing(wall, [a.elapsed_time(b) for a, b in evs], kern)
 
@@ -367,9 +375,8 @@ def main():
     tl.load()
 
     head, inp, S = bench_prefill(8192, synth.DT_BF16, args.seed, args.steps, args.warmup)
-    # the headline inputs stay on the host for the CPU baseline; freed on the
-    # device before the other workloads (kept there, they made the first fp8
-    # call sequence measure ~2x its GPU time in wall-clock terms)
+    # the headline inputs stay on the host for the CPU baseline and are freed
+    # on the device before the other workloads
     inp = synth.IndexerPrefill(inp.dt, inp.q.cpu(), None if inp.q_scale is None else inp.q_scale.cpu(), inp.k.cpu(),
                                None if inp.k_scale is None else inp.k_scale.cpu(), inp.w.cpu(), inp.probes)
     del S
