@@ -329,8 +329,8 @@ TRAFFIC_SOURCES = ("indexer.hip", "tlsl_device.h", "tlsl_internal.h", "topk_comm
 TRAFFIC = {
     # profiles/prefill_score_kernel_bf16_n8192.md
     "prefill_score_kernel": {
-        "sources_sha256": "dc6ecec084966f6eff9af5a12c1dedd67bdcd20822b2ed3ecda590ff5fb2f1ed",
-        "fetch_kib": 85515.1562, "write_kib": 158356.2969,
+        "sources_sha256": "a280d85f92863a74cfa1f390ab42d7e910e781b4aed61bb83218fe24695bc835",
+        "fetch_kib": 85355.0312, "write_kib": 168479.3203,
         "copy_fetch_kib": 524313.5357, "copy_write_kib": 1048576.0, "copy_bytes": 1 << 30,
     },
 }
