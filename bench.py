@@ -190,7 +190,7 @@ def decode_stage_bytes(lengths, HI, DI, H, Dqk, Dv, k):
         # K^I cache + scales, queries + scale + weights, scores out
         "decode_scan_kernel": float((L * (DI + 4 + 4)).sum() + B * (HI * DI + 4 + 4 * HI)),
         # scores in (full rows), S out
-        "topk_row_kernel": float((L * 4).sum() + B * k * 4),
+        "topk_filter_kernel": float((L * 4).sum() + B * k * 4),
         # gathered entries, queries, S, outputs
         "sparse_attn_kernel": float((K * Dqk * 2).sum() + B * H * Dqk * 2 + B * k * 4 + B * H * Dv * 2),
     }
@@ -234,7 +234,8 @@ def bench_decode(seed, steps, warmup):
     sbytes = decode_stage_bytes(lengths, HI, DI, H, Dqk, Dv, k)
     stages = {}
     for name, fn, kerns in (("index_decode", f_index, ("decode_scan_kernel",)),
-                            ("topk_select", f_topk, ("topk_row_kernel",)),
+                            ("topk_select", f_topk, ("topk_threshold_kernel", "topk_filter_kernel",
+                                                     "topk_final_kernel")),
                             ("sparse_attn_decode", f_attn, ("sparse_attn_kernel", "attn_combine_kernel"))):
         st = None
         kd = {}

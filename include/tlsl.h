@@ -124,8 +124,7 @@ int index_decode(const void* qI, const float* q_scale, const void* kI_cache,
  *   row_start [R] int64 (device), row_len [R] int32 (device, >= 0)
  *   max_len   >= every row_len (host value)
  *   S         [R,k] int32 out, S_score [R,k] fp32 out (optional)
- *   workspace 256 bytes, unused (query protocol above; kept so that a
- *             later method may use scratch memory without an ABI change)
+ *   workspace about R*(2k+264)*8 bytes (query protocol above)
  * Supported: 1 <= k <= 4096, 0 <= row_len < 2^31.
  */
 int topk_select(const float* scores, const int64_t* row_start, const int32_t* row_len, int R,

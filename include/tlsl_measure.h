@@ -22,7 +22,7 @@ extern "C" {
 
 /* Arms the kernel timer for the kernel named `kernel` (its function name
  * without namespace or template arguments, e.g. "prefill_score_kernel",
- * "decode_scan_kernel", "sparse_attn_kernel", "topk_row_kernel").  From
+ * "decode_scan_kernel", "sparse_attn_kernel", "topk_filter_kernel").  From
  * then on, each launch of that kernel by any entry point is bracketed by a
  * pair of HIP events recorded on the launch stream, for at most
  * `max_launches` (1..65536) launches; later launches are not timed.  Events

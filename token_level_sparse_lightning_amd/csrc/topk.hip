@@ -2,18 +2,18 @@
 // (DSA page, section 1.1 eq.(2); section 2 on radix top-k over rows given by
 // sequence lengths, avoiding a full sort).
 //
-// One workgroup per row, in one launch:
-//  1. the r-th largest of a strided sample of the row (r = expected sample
-//     hits inside the top-k plus 4 standard deviations) -- a conservative
-//     threshold;
-//  2. every (score, position) of the row at or above it is appended to LDS
-//     (16-byte loads, one LDS counter increment per wave and load);
-//  3. an exact radix select among those candidates, ties resolved to the
-//     lowest positions, and the selected positions written in ascending order
-//     through a position bitmap.
-// A row whose candidates miss (the sample threshold overshot) or overflow is
-// selected from its full score row instead (topk_common.h).  The result never
-// depends on the threshold, only the work does.
+// Three launches, every one spread over many workgroups:
+//  1. topk_threshold: per row, the r-th largest of a strided sample of the
+//     row (r = expected sample hits inside the top-k plus 4 standard
+//     deviations) -- a conservative threshold.
+//  2. topk_filter: workgroups over (row chunk) append every (score, position)
+//     at or above the row's threshold to the row's candidate buffer.
+//  3. topk_final: per row, an exact radix select among the candidates in LDS,
+//     ties resolved to the lowest positions, and the selected positions
+//     written in ascending order through a position bitmap.  A row whose
+//     candidates miss (the sample threshold overshot) or overflow is selected
+//     from its full score row instead (topk_common.h).
+// The result never depends on the threshold, only the work does.
 #include <math.h>
 
 #include "tlsl_device.h"
@@ -22,11 +22,15 @@
 
 namespace tlsl {
 
-constexpr int TR_NT = 1024;              // workgroup (one row)
-constexpr int TT_SAMPLE_MAX = 8192;      // sample values held in LDS
-constexpr int TSEL_CAPMAX = 8448;        // candidates held in LDS, max
-constexpr int TSEL_BITMAP_WORDS = 4096;  // rows up to 131072 use the bitmap output
-constexpr int TR_BATCH = 8;              // 16-byte loads in flight per thread
+constexpr int TT_NT = 1024;             // threshold workgroup
+constexpr int TT_SAMPLE_MAX = 8192;     // sample values held in LDS
+constexpr int TF_NT = 256;              // filter workgroup
+constexpr int TF_PER = 16;              // scores per filter thread
+constexpr int TF_CHUNK = TF_NT * TF_PER;
+constexpr int TFIN_NT = 1024;           // final workgroup
+constexpr int TSEL_CAPMAX = 8448;       // candidate buffer entries per row, max
+constexpr int TSEL_BITMAP_WORDS = 4096; // rows up to 131072 use the bitmap output
+constexpr int TSEL_CNT_STRIDE = 32;   // one 128-byte line per row counter
 constexpr float TSEL_SIGMA = 4.0f;
 
 struct TopkArgs {
@@ -34,6 +38,9 @@ struct TopkArgs {
     const int64_t* row_start;
     const int32_t* row_len;
     int k, cap;
+    float* theta;   // [R]
+    int* cnt;       // [R]
+    uint2* buf;     // [R][cap]
     int32_t* S;
     float* Ss;
 };
@@ -60,146 +67,149 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, int* scratch) 
 
 __device__ __forceinline__ int sample_stride(int L) { return max(16, (L + TT_SAMPLE_MAX - 1) / TT_SAMPLE_MAX); }
 
-struct TopkRowSmem {
-    uint32_t keys[TSEL_CAPMAX];  // the sample's keys, then the candidates' keys
+__global__ __launch_bounds__(TT_NT) void topk_threshold_kernel(TopkArgs a) {
+    __shared__ uint32_t skeys[TT_SAMPLE_MAX];
+    __shared__ SelectSmem sel;
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int L = max(a.row_len[r], 0);
+    if (tid == 0) a.cnt[r * TSEL_CNT_STRIDE] = 0;
+    const int K = min(a.k, L);
+    const int stride = sample_stride(L);
+    const int ns = L > 0 ? (L - 1) / stride + 1 : 0;
+    const float mu = L > 0 ? (float)ns * (float)K / (float)L : 0.f;
+    const int need = (int)ceilf(mu + TSEL_SIGMA * sqrtf(mu)) + 2;
+    if (L <= a.cap || need >= ns) {
+        if (tid == 0) a.theta[r] = -INFINITY;
+        return;
+    }
+    const float* sc = a.scores + a.row_start[r];
+    batched_copy<TT_NT, 16>(ns, [&](int j) { return sc[(size_t)j * stride]; },
+                            [&](int j, float v) { skeys[j] = score_key(v); });
+    __syncthreads();
+    int gt;
+    const uint32_t T = block_select_adaptive<TT_NT>(ns, need, [&](int i, bool* ok) { *ok = true; return skeys[i]; },
+                                                    sel, &gt);
+    if (tid == 0) a.theta[r] = key_score(T);
+}
+
+__global__ __launch_bounds__(TF_NT) void topk_filter_kernel(TopkArgs a) {
+    const int r = blockIdx.y;
+    const int L = max(a.row_len[r], 0);
+    const int base = blockIdx.x * TF_CHUNK;
+    if (base >= L) return;
+    __shared__ int wsum[TF_NT / 64 + 1];
+    const float th = a.theta[r];
+    const float* sc = a.scores + a.row_start[r];
+    uint2* out = a.buf + (size_t)r * a.cap;
+    const int w = threadIdx.x >> 6;
+    float v[TF_PER];
+#pragma unroll
+    for (int i = 0; i < TF_PER; ++i) {
+        const int idx = base + i * TF_NT + threadIdx.x;
+        v[i] = idx < L ? sc[idx] : -INFINITY;
+    }
+    // count first, then reserve the workgroup's slots with a single atomic
+    uint64_t m[TF_PER];
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < TF_PER; ++i) {
+        const int idx = base + i * TF_NT + threadIdx.x;
+        m[i] = ballot(idx < L && v[i] >= th);
+        mine += __popcll(m[i]);
+    }
+    if (lane_id() == 0) wsum[w] = mine;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int tot = 0;
+        for (int i = 0; i < TF_NT / 64; ++i) tot += wsum[i];
+        wsum[TF_NT / 64] = tot > 0 ? atomicAdd(&a.cnt[r * TSEL_CNT_STRIDE], tot) : 0;
+    }
+    __syncthreads();
+    int slot = wsum[TF_NT / 64];
+    for (int i = 0; i < w; ++i) slot += wsum[i];
+#pragma unroll
+    for (int i = 0; i < TF_PER; ++i) {
+        const int idx = base + i * TF_NT + threadIdx.x;
+        const bool ok = (m[i] >> lane_id()) & 1ull;
+        const int s = slot + rank_below(m[i]);
+        if (ok && s < a.cap) out[s] = make_uint2(__float_as_uint(v[i]), (uint32_t)idx);
+        slot += __popcll(m[i]);
+    }
+}
+
+struct TopkFinalSmem {
+    uint32_t keys[TSEL_CAPMAX];
     uint32_t pos[TSEL_CAPMAX];
     uint32_t bitmap[TSEL_BITMAP_WORDS];
     SelectSmem sel;
-    int cnt, nties;
+    int nties;
 };
 
-union TopkRowShared {
-    TopkRowSmem f;
+union TopkFinalShared {
+    TopkFinalSmem f;
     TopkSmem g;
 };
 
-__global__ __launch_bounds__(TR_NT) void topk_row_kernel(TopkArgs a) {
-    __shared__ TopkRowShared sh;
-    TopkRowSmem& s = sh.f;
-    const int r = blockIdx.x, tid = threadIdx.x, l = lane_id();
+__global__ __launch_bounds__(TFIN_NT) void topk_final_kernel(TopkArgs a) {
+    __shared__ TopkFinalShared sh;
+    const int r = blockIdx.x, tid = threadIdx.x;
     const int L = max(a.row_len[r], 0);
     const int K = min(a.k, L);
     const float* sc = a.scores + a.row_start[r];
     int32_t* Srow = a.S + (size_t)r * a.k;
     float* Ssrow = a.Ss ? a.Ss + (size_t)r * a.k : nullptr;
+    const int cnt = a.cnt[r * TSEL_CNT_STRIDE];
+    const int nwords = (L + 31) / 32;
+    if (L > a.k && (cnt < K || cnt > a.cap || nwords > TSEL_BITMAP_WORDS)) {
+        block_topk_row<TFIN_NT>(sc, L, a.k, Srow, Ssrow, sh.g);
+        return;
+    }
     if (L <= a.k) {
-        for (int i = tid; i < a.k; i += TR_NT) {
+        for (int i = tid; i < a.k; i += TFIN_NT) {
             Srow[i] = i < L ? i : -1;
             if (Ssrow) Ssrow[i] = i < L ? sc[i] : -INFINITY;
         }
         return;
     }
-    const int nwords = (L + 31) / 32;
-    // ---- 1. sample threshold (rows within the candidate capacity keep all) --
-    float theta = -INFINITY;
-    {
-        const int stride = sample_stride(L);
-        const int ns = (L - 1) / stride + 1;
-        const float mu = (float)ns * (float)K / (float)L;
-        const int need = (int)ceilf(mu + TSEL_SIGMA * sqrtf(mu)) + 2;
-        if (L > a.cap && need < ns) {
-            batched_copy<TR_NT, 16>(ns, [&](int j) { return sc[(size_t)j * stride]; },
-                                    [&](int j, float v) { s.keys[j] = score_key(v); });
-            __syncthreads();
-            int gt;
-            const uint32_t T = block_select_adaptive<TR_NT>(
-                ns, need, [&](int i, bool* ok) { *ok = true; return s.keys[i]; }, s.sel, &gt);
-            theta = key_score(T);
-        }
-    }
-    // ---- 2. candidates: every score >= theta, appended to LDS ---------------
-    // 16-byte loads from the first 16-byte boundary of the row (the head
-    // before it and the tail after the last whole float4, fewer than 4 scores
-    // each, go to the first threads with the first batch); per batch each
-    // thread counts its hits, one workgroup scan gives every thread its slots
-    {
-        const int head = min(L, (int)(((16 - ((uintptr_t)sc & 15)) & 15) / 4));
-        const float4* v4 = reinterpret_cast<const float4*>(sc + head);
-        const int n4 = (L - head) / 4;
-        const int tail0 = head + 4 * n4;
-        int base = 0;
-        for (int b0 = 0; b0 == 0 || b0 < n4; b0 += TR_NT * TR_BATCH) {
-            float4 v[TR_BATCH];
-#pragma unroll
-            for (int u = 0; u < TR_BATCH; ++u) {
-                const int i = b0 + u * TR_NT + tid;
-                v[u] = i < n4 ? v4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-            }
-            // the scalar extras: thread t < 4 takes head score t and tail score t
-            float xh = -INFINITY, xt = -INFINITY;
-            if (b0 == 0 && tid < 4) {
-                if (tid < head) xh = sc[tid];
-                if (tail0 + tid < L) xt = sc[tail0 + tid];
-            }
-            int mine = (xh >= theta) + (xt >= theta);
-#pragma unroll
-            for (int u = 0; u < TR_BATCH; ++u)
-                mine += (v[u].x >= theta) + (v[u].y >= theta) + (v[u].z >= theta) + (v[u].w >= theta);
-            int total;
-            int o = base + block_excl_scan<TR_NT>(mine, &total, s.sel.scratch);
-            auto put = [&](float x, int p) {
-                if (x >= theta) {
-                    if (o < TSEL_CAPMAX) {
-                        s.keys[o] = score_key(x);
-                        s.pos[o] = (uint32_t)p;
-                    }
-                    ++o;
-                }
-            };
-            put(xh, tid);
-            put(xt, tail0 + tid);
-#pragma unroll
-            for (int u = 0; u < TR_BATCH; ++u) {
-                const int p = head + 4 * (b0 + u * TR_NT + tid);
-                put(v[u].x, p);
-                put(v[u].y, p + 1);
-                put(v[u].z, p + 2);
-                put(v[u].w, p + 3);
-            }
-            base += total;
-        }
-        if (tid == 0) s.cnt = base;
-    }
-    __syncthreads();
-    const int cnt = s.cnt;
-    if (cnt < K || cnt > min(a.cap, TSEL_CAPMAX) || nwords > TSEL_BITMAP_WORDS) {
-        __syncthreads();  // every thread has read cnt before the union is reused
-        block_topk_row<TR_NT>(sc, L, a.k, Srow, Ssrow, sh.g);
-        return;
-    }
-    // ---- 3. exact selection among the candidates ---------------------------
-    for (int i = tid; i < nwords; i += TR_NT) s.bitmap[i] = 0u;
+    TopkFinalSmem& s = sh.f;
+    const uint2* src = a.buf + (size_t)r * a.cap;
+    if (cnt > 0)
+        batched_copy<TFIN_NT, 8>(cnt, [&](int i) { return src[i]; }, [&](int i, uint2 e) {
+            s.keys[i] = score_key(__uint_as_float(e.x));
+            s.pos[i] = e.y;
+        });
+    for (int i = tid; i < nwords; i += TFIN_NT) s.bitmap[i] = 0u;
     if (tid == 0) s.nties = 0;
     __syncthreads();
     int gt;
-    const uint32_t T = block_select_adaptive<TR_NT>(cnt, K, [&](int i, bool* ok) { *ok = true; return s.keys[i]; },
-                                                    s.sel, &gt);
+    const uint32_t T = block_select_adaptive<TFIN_NT>(cnt, K, [&](int i, bool* ok) { *ok = true; return s.keys[i]; },
+                                                      s.sel, &gt);
     // ties at T: keep the (K - gt) lowest positions, i.e. the largest inverted
     // positions; when every tie is kept no selection is needed
     const int need_ties = K - gt;
     int nt_local = 0;
-    for (int i = tid; i < cnt; i += TR_NT) nt_local += s.keys[i] == T;
+    for (int i = tid; i < cnt; i += TFIN_NT) nt_local += s.keys[i] == T;
     nt_local = wave_sum(nt_local);
-    if (l == 0 && nt_local) atomicAdd(&s.nties, nt_local);
+    if (lane_id() == 0 && nt_local) atomicAdd(&s.nties, nt_local);
     __syncthreads();
     uint32_t inv_cut = 0u;
     if (s.nties > need_ties) {
         int tgt;
-        inv_cut = block_select_adaptive<TR_NT>(
+        inv_cut = block_select_adaptive<TFIN_NT>(
             cnt, need_ties, [&](int i, bool* ok) { *ok = s.keys[i] == T; return ~s.pos[i]; }, s.sel, &tgt);
     }
-    for (int i = tid; i < cnt; i += TR_NT) {
+    for (int i = tid; i < cnt; i += TFIN_NT) {
         const uint32_t key = s.keys[i];
         if (key > T || (key == T && ~s.pos[i] >= inv_cut)) atomicOr(&s.bitmap[s.pos[i] >> 5], 1u << (s.pos[i] & 31));
     }
     __syncthreads();
     // ordered output: each thread owns a contiguous run of bitmap words
-    const int per = (nwords + TR_NT - 1) / TR_NT;
+    const int per = (nwords + TFIN_NT - 1) / TFIN_NT;
     const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
     int mine = 0;
     for (int wd = w0; wd < w1; ++wd) mine += __popc(s.bitmap[wd]);
     int total;
-    int o = block_excl_scan<TR_NT>(mine, &total, s.sel.scratch);
+    int o = block_excl_scan<TFIN_NT>(mine, &total, s.sel.scratch);
     for (int wd = w0; wd < w1; ++wd) {
         uint32_t bits = s.bitmap[wd];
         while (bits) {
@@ -211,29 +221,39 @@ __global__ __launch_bounds__(TR_NT) void topk_row_kernel(TopkArgs a) {
             ++o;
         }
     }
-    for (int i = K + tid; i < a.k; i += TR_NT) {
+    for (int i = K + tid; i < a.k; i += TFIN_NT) {
         Srow[i] = -1;
         if (Ssrow) Ssrow[i] = -INFINITY;
     }
 }
 
-static int topk_cap(int k) { return std::min(TSEL_CAPMAX, (int)((2 * (size_t)k + 256 + 255) / 256 * 256)); }
+static int topk_cap(int k) { return (int)((2 * (size_t)k + 256 + 255) / 256 * 256); }
 
-size_t topk_ws_bytes(int, int, int) { return 256; }  // none needed; never empty (a NULL workspace is a size query)
+static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t topk_ws_bytes(int R, int k, int) {
+    return a256((size_t)R * sizeof(float)) + a256((size_t)R * TSEL_CNT_STRIDE * sizeof(int)) + a256((size_t)R * topk_cap(k) * sizeof(uint2));
+}
 
 hipError_t launch_topk_select(const float* scores, const int64_t* row_start, const int32_t* row_len, int R, int k,
                               int max_len, int32_t* S, float* S_score, void* ws, hipStream_t st) {
-    (void)max_len;
-    (void)ws;
+    unsigned char* w = static_cast<unsigned char*>(ws);
     TopkArgs a;
     a.scores = scores;
     a.row_start = row_start;
     a.row_len = row_len;
     a.k = k;
     a.cap = topk_cap(k);
+    a.theta = reinterpret_cast<float*>(w);
+    a.cnt = reinterpret_cast<int*>(w + a256((size_t)R * sizeof(float)));
+    a.buf = reinterpret_cast<uint2*>(w + a256((size_t)R * sizeof(float)) + a256((size_t)R * TSEL_CNT_STRIDE * sizeof(int)));
     a.S = S;
     a.Ss = S_score;
-    TLSL_TIMED_LAUNCH("topk_row_kernel", st, hipLaunchKernelGGL(topk_row_kernel, dim3(R), dim3(TR_NT), 0, st, a));
+    TLSL_TIMED_LAUNCH("topk_threshold_kernel", st, hipLaunchKernelGGL(topk_threshold_kernel, dim3(R), dim3(TT_NT), 0, st, a));
+    const int chunks = max_len > 0 ? (max_len + TF_CHUNK - 1) / TF_CHUNK : 1;
+    TLSL_TIMED_LAUNCH("topk_filter_kernel", st,
+                      hipLaunchKernelGGL(topk_filter_kernel, dim3(chunks, R), dim3(TF_NT), 0, st, a));
+    TLSL_TIMED_LAUNCH("topk_final_kernel", st, hipLaunchKernelGGL(topk_final_kernel, dim3(R), dim3(TFIN_NT), 0, st, a));
     return hipGetLastError();
 }
 
