@@ -26,7 +26,9 @@ F32, BF16, FP8 = synth.DT_F32, synth.DT_BF16, synth.DT_FP8
 # ---------------------------------------------------------------------------
 def _score_rows(seed):
     rng = np.random.default_rng(seed)
-    lens = [0, 1, 5, 63, 64, 65, 100, 1000, 2047, 2048, 2049, 5000, 4000, 3500, 20000, 20000, 9000]
+    # (140001: several load batches per row, and past the position bitmap of the
+    # in-LDS path, so it is selected from the full row)
+    lens = [0, 1, 5, 63, 64, 65, 100, 1000, 2047, 2048, 2049, 140001, 5000, 4000, 3500, 20000, 20000, 9000]
     rows = []
     for i, L in enumerate(lens):
         if i in (len(lens) - 5, len(lens) - 4):
