@@ -61,7 +61,7 @@ __global__ __launch_bounds__(CC_NT) void calib_copy_kernel(const uint4* __restri
 #pragma unroll
         for (int u = 0; u < CC_UNROLL; ++u) {
             const size_t i = base + (size_t)u * CC_NT;
-            if (i < n) v[u] = src[i];
+            v[u] = i < n ? src[i] : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
         for (int u = 0; u < CC_UNROLL; ++u) {
