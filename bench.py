@@ -331,8 +331,8 @@ TRAFFIC = {
     # profiles/prefill_score_kernel_bf16_n8192.md
     "prefill_score_kernel": {
         "sources_sha256": "a280d85f92863a74cfa1f390ab42d7e910e781b4aed61bb83218fe24695bc835",
-        "fetch_kib": 85355.0312, "write_kib": 168479.3203,
-        "copy_fetch_kib": 524313.5357, "copy_write_kib": 1048576.0, "copy_bytes": 1 << 30,
+        "fetch_kib": 85369.125, "write_kib": 168479.7422,
+        "copy_fetch_kib": 524302.1518, "copy_write_kib": 1048576.0, "copy_bytes": 1 << 30,
     },
 }
 
