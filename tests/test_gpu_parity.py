@@ -74,7 +74,7 @@ def test_topk_select_exact(k):
 @pytest.mark.parametrize("dt", [F32, BF16, FP8])
 def test_index_decode(dt):
     HI, DI = (4, 32) if dt == F32 else (64, 128)
-    lengths = [1, 17, 64, 65, 300, 2048, 2049, 5000]
+    lengths = [1, 0, 17, 64, 65, 300, 0, 2048, 2049, 5000]  # empty sequences are skipped
     dist = "dyadic" if dt == F32 else "normal"
     # planted keys carry N(0,1) noise, so the exact (dyadic) case plants none
     inp = synth.indexer_decode(lengths, HI, DI, dt, seed=3, dist=dist, planted=dt != F32)
@@ -289,7 +289,7 @@ def test_sparse_attn_prefill_empty_rows():
 
 @pytest.mark.parametrize("dt,H,Dqk,Dv", [(BF16, 128, 576, 512), (F32, 4, 80, 64)])
 def test_sparse_attn_decode(dt, H, Dqk, Dv):
-    lengths = [1, 5, 64, 2048, 3000, 5000]
+    lengths = [1, 0, 5, 64, 2048, 3000, 5000]  # an empty sequence: zero output, lse -inf
     k = 2048
     q, kv = synth.attn_decode(lengths, H, Dqk, dt, seed=13)
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
