@@ -733,6 +733,17 @@ __global__ __launch_bounds__(DEC_NT) void decode_score_kernel(const unsigned cha
 // of work and no workgroup is launched for keys past a sequence's end.
 constexpr int DEC2_NT = 256;
 constexpr int DEC2_MAXB = 4096;
+// Dynamic LDS: the subtile prefix and sequence starts of the batch, then the
+// staged scores -- the workgroup's whole range when it fits (written by the
+// workgroup at the end, mostly with 16-byte stores), else a stage per wave
+// (written at the end of each sequence run or when full).  Stored per subtile
+// in between the key loads, the 256-byte score stores cost 22 of 135 us at
+// 64 sequences; staged, about half of that.
+constexpr size_t DEC2_LDS_BUDGET = 78 * 1024;  // per workgroup (two resident per CU)
+__host__ __device__ constexpr size_t dec2_off_sstart(int B) { return ((size_t)(B + 1) * 4 + 7) & ~(size_t)7; }
+__host__ __device__ constexpr size_t dec2_off_stage(int B) {
+    return (dec2_off_sstart(B) + (size_t)(B + 1) * 8 + 15) & ~(size_t)15;
+}
 
 __device__ __forceinline__ int find_seq(const int* pre, int B, int g) {
     int lo = 0, hi = B;  // pre[lo] <= g < pre[hi]
@@ -748,16 +759,24 @@ template <int DT, int HB, int DI>
 __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned char* q, const float* q_scale,
                                                               const unsigned char* kc, const float* k_scale,
                                                               const float* w, const int64_t* cu, int B, int HI,
-                                                              float* scores) {
+                                                              float* scores, int scap, int stage_sub) {
     using I = Idx<DT, HB, DI>;
     constexpr int NCH = I::NCH;
     constexpr int NWV = DEC2_NT / 64;
-    __shared__ int pre[DEC2_MAXB + 1];
-    __shared__ int64_t sstart[DEC2_MAXB + 1];
+    extern __shared__ __align__(16) unsigned char dsm[];
+    int* pre = reinterpret_cast<int*>(dsm);
+    int64_t* sstart = reinterpret_cast<int64_t*>(dsm + dec2_off_sstart(B));
     __shared__ int scratch[16];
     // (wave index as a scalar: the subtile loop is then uniform, and the
     // compiler adds no wait for all loads at its head)
     const int tid = threadIdx.x, wv_id = __builtin_amdgcn_readfirstlane(tid >> 6), l = lane_id();
+    // scap > 0: each wave stages up to scap subtiles; scap == 0: the range of
+    // the workgroup is staged (subtile g at (g - g0) * 64; stage_sub subtiles
+    // at most, which covers the range whenever max_len bounds the lengths as
+    // required; past it scores are stored directly) and written by the
+    // workgroup at the end with 16-byte stores
+    float* const stage = reinterpret_cast<float*>(dsm + dec2_off_stage(B));
+    float* sb = stage + (size_t)wv_id * scap * 64;
     // subtile prefix over the sequences, and the sequence starts
     int carry = 0;
     for (int b0 = 0; b0 < B; b0 += DEC2_NT) {
@@ -790,9 +809,9 @@ __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned cha
     // (segment) at a time so that the inner loop has straight-line loads.  A
     // subtile's keys and key scales are loaded one step before its scores:
     // both are loop-carried, so the compiler cannot sink the scale load next
-    // to the score store (where its wait would also wait for the prefetch).
-    // Loads past the segment end are clamped to its last key (in bounds,
-    // unused).
+    // to a store.  Loads past the segment end are clamped to its last key (in
+    // bounds, unused).  Scores go to the wave's stage in LDS and out at the
+    // end of the segment (or when the stage is full).
     int g = g0 + wv_id;
     while (g < g1) {
         const int b = find_seq(pre, B, g);
@@ -808,10 +827,25 @@ __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned cha
             ks_ = DT == kFP8 ? k_scale[start + min(k0 + l, L - 1)] : 1.f;
         };
         fetch(key0, kf[0], ksc[0]);
+        int nst = 0, st_key0 = key0;  // staged subtiles and the first one's key
+        auto flush = [&] {
+            for (int k = 0; k < nst; ++k) {
+                const int key = st_key0 + 64 * NWV * k + l;
+                if (key < L) scores[start + key] = sb[64 * k + l];
+            }
+            nst = 0;
+        };
         auto step = [&](const uint4 (&cur)[4][NCH], float ks, uint4 (&ahead)[4][NCH], float& ks_ahead) {
             fetch(key0 + 64 * NWV, ahead, ks_ahead);
             const float s = I::score_lean(qf, wv, cur) * ks;
-            if (key0 + l < L) scores[start + key0 + l] = s;
+            if (scap == 0) {
+                if (g - g0 < stage_sub) stage[(size_t)(g - g0) * 64 + l] = s;
+                else if (key0 + l < L) scores[start + key0 + l] = s;
+            } else {
+                if (nst == 0) st_key0 = key0;
+                sb[64 * nst + l] = s;
+                if (++nst == scap) flush();
+            }
             g += NWV;
             key0 += 64 * NWV;
             return g < seg_end;
@@ -819,6 +853,33 @@ __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned cha
         for (;;) {
             if (!step(kf[0], ksc[0], kf[1], ksc[1])) break;
             if (!step(kf[1], ksc[1], kf[0], ksc[0])) break;
+        }
+        if (scap > 0) flush();
+    }
+    if (scap == 0 && g0 < g1) {
+        // the workgroup's staged range, one contiguous run per sequence: a
+        // head of up to 3 scores to the next 16-byte boundary, 16-byte
+        // stores, a tail
+        __syncthreads();
+        for (int b = find_seq(pre, B, g0); b < B && pre[b] < g1; ++b) {
+            const int gs = max(g0, pre[b]), ge = min(min(g1, g0 + stage_sub), pre[b + 1]);
+            if (gs >= ge) continue;
+            const int64_t start = sstart[b];
+            const int L = (int)(sstart[b + 1] - start);
+            const int kfirst = (gs - pre[b]) * 64;
+            const int n = min(L, (ge - pre[b]) * 64) - kfirst;
+            const float* src = stage + (size_t)(gs - g0) * 64;
+            float* dst = scores + start + kfirst;
+            const int head = min(n, (int)((4 - ((start + kfirst) & 3)) & 3));
+            if (tid < head) dst[tid] = src[tid];
+            const int m = (n - head) >> 2;
+            float4* d4 = reinterpret_cast<float4*>(dst + head);
+            for (int i = tid; i < m; i += DEC2_NT) {
+                const float* v = src + head + 4 * i;
+                d4[i] = make_float4(v[0], v[1], v[2], v[3]);
+            }
+            const int t0 = head + 4 * m;
+            if (t0 + tid < n) dst[t0 + tid] = src[t0 + tid];
         }
     }
 }
@@ -975,21 +1036,30 @@ static hipError_t launch_decode_t(const void* q, const float* q_scale, const voi
                                   const float* w, const int64_t* cu, int B, int HI, int max_len, float* scores,
                                   hipStream_t st) {
     if (B <= DEC2_MAXB) {
-        // enough resident workgroups to fill every CU a few times over; each
-        // gets an equal share of the batch's subtiles
-        static int per_cu = 0;  // resident workgroups per CU for this instantiation
-        if (per_cu == 0) {
-            int nb = 0;
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_scan_kernel<DT, HB, DI>, DEC2_NT, 0) != hipSuccess ||
-                nb <= 0)
-                nb = 2;
-            per_cu = nb;
-        }
-        const int grid = std::min(device_cu_count() * per_cu, std::max(1, (int)(((int64_t)max_len * B + 63) / 64)));
+        // resident workgroups per CU: two where the registers allow (the LDS
+        // stays within DEC2_LDS_BUDGET), each with an equal share of the
+        // batch's subtiles; the stage holds a workgroup's whole share when it
+        // fits, else a share per wave (flushed when full)
+        constexpr int NWV = DEC2_NT / 64;
+        const int64_t nsub_max = (int64_t)B * ((max_len + 63) / 64);
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_scan_kernel<DT, HB, DI>, DEC2_NT,
+                                                         DEC2_LDS_BUDGET) != hipSuccess ||
+            nb < 1)
+            nb = 1;
+        const int grid = (int)std::min<int64_t>((int64_t)device_cu_count() * std::min(nb, 2), std::max<int64_t>(1, nsub_max));
+        const int64_t per_max = (nsub_max + grid - 1) / grid;  // >= every workgroup's share
+        const int64_t pw_max = (per_max + NWV - 1) / NWV;
+        const size_t base = dec2_off_stage(B);
+        const bool wg_stage = base + (size_t)per_max * 256 <= DEC2_LDS_BUDGET;
+        const int scap =
+            wg_stage ? 0 : (int)std::max<int64_t>(1, std::min<int64_t>(pw_max, (DEC2_LDS_BUDGET - base) / (NWV * 256)));
+        const size_t dyn = wg_stage ? base + (size_t)per_max * 256 : base + (size_t)NWV * scap * 256;
         TLSL_TIMED_LAUNCH("decode_scan_kernel", st,
-                          hipLaunchKernelGGL((decode_scan_kernel<DT, HB, DI>), dim3(grid), dim3(DEC2_NT), 0, st,
+                          hipLaunchKernelGGL((decode_scan_kernel<DT, HB, DI>), dim3(grid), dim3(DEC2_NT), dyn, st,
                                              static_cast<const unsigned char*>(q), q_scale,
-                                             static_cast<const unsigned char*>(kc), k_scale, w, cu, B, HI, scores));
+                                             static_cast<const unsigned char*>(kc), k_scale, w, cu, B, HI, scores,
+                                             scap, (int)(wg_stage ? per_max : 0)));
         return hipGetLastError();
     }
     dim3 grid((max_len + DEC_CHUNK - 1) / DEC_CHUNK, B);
