@@ -71,16 +71,19 @@ def test_topk_select_exact(k):
 # ---------------------------------------------------------------------------
 # index_decode
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dt", [F32, BF16, FP8])
-def test_index_decode(dt):
+@pytest.mark.parametrize("dt,max_len", [(F32, None), (BF16, None), (FP8, None), (FP8, 4_000_000)])
+def test_index_decode(dt, max_len):
+    """max_len far above the lengths (allowed: it only has to bound them) sizes
+    the launch for long sequences, so each wave stages its own scores instead
+    of the workgroup staging its whole range."""
     HI, DI = (4, 32) if dt == F32 else (64, 128)
     lengths = [1, 0, 17, 64, 65, 300, 0, 2048, 2049, 5000]  # empty sequences are skipped
     dist = "dyadic" if dt == F32 else "normal"
     # planted keys carry N(0,1) noise, so the exact (dyadic) case plants none
     inp = synth.indexer_decode(lengths, HI, DI, dt, seed=3, dist=dist, planted=dt != F32)
-    announce(f"index_decode dt={dt}")
+    announce(f"index_decode dt={dt} max_len={max_len}")
     sc = tl.index_decode(to_dev(inp.q), to_dev(inp.k), to_dev(inp.w), to_dev(inp.cu_seqlens),
-                         max(lengths), q_scale=to_dev(inp.q_scale), k_scale=to_dev(inp.k_scale))
+                         max_len or max(lengths), q_scale=to_dev(inp.q_scale), k_scale=to_dev(inp.k_scale))
     torch.cuda.synchronize()
     ref, mag = oracle.index_decode(dt, host(inp.q), host(inp.q_scale), host(inp.k), host(inp.k_scale),
                                    host(inp.w), host(inp.cu_seqlens))
