@@ -330,9 +330,9 @@ TRAFFIC_SOURCES = ("indexer.hip", "tlsl_device.h", "tlsl_internal.h", "topk_comm
 TRAFFIC = {
     # profiles/prefill_score_kernel_bf16_n8192.md
     "prefill_score_kernel": {
-        "sources_sha256": "a280d85f92863a74cfa1f390ab42d7e910e781b4aed61bb83218fe24695bc835",
-        "fetch_kib": 85369.125, "write_kib": 168479.7422,
-        "copy_fetch_kib": 524302.1518, "copy_write_kib": 1048576.0, "copy_bytes": 1 << 30,
+        "sources_sha256": "8c03ea05c6a6787667b9d20ab65d20801fe71e1dd39da3a87cc621f7cd686e8e",
+        "fetch_kib": 85341.2656, "write_kib": 168479.4141,
+        "copy_fetch_kib": 524302.0982, "copy_write_kib": 1048576.0, "copy_bytes": 1 << 30,
     },
 }
 
