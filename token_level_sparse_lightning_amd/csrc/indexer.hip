@@ -521,12 +521,16 @@ struct FinalizeArgs {
 
 template <int CAPMAX>
 __global__ __launch_bounds__(FIN_NT) void prefill_finalize_kernel(FinalizeArgs a) {
-    // order-preserving keys in ascending position order; the positions are
-    // read back from the candidate buffer (L2-resident) when the selection is
-    // written, so that four workgroups fit per CU
-    __shared__ uint32_t fkey[CAPMAX];
+    // Candidate i of a row, in ascending position order (buffer entry cnt-1-i:
+    // the buffer holds descending positions), is held in registers by thread
+    // i % FIN_NT as its (i / FIN_NT)-th item: one coalesced read of the buffer
+    // gives both the score keys for the selection and the positions for S.
+    constexpr int SEG = (CAPMAX + FIN_NT - 1) / FIN_NT;
+    constexpr int NW = FIN_NT / 64;
+    constexpr int NE = SEG * NW;  // (item, wave) groups, in candidate order
     __shared__ SelectSmem sel;
-    const int tid = threadIdx.x;
+    __shared__ int gcnt[2][NE];
+    const int tid = threadIdx.x, w = tid >> 6;
     const int row = blockIdx.x;
     const int t = row % a.n;
     const int K = min(a.topk, t + 1);
@@ -536,50 +540,86 @@ __global__ __launch_bounds__(FIN_NT) void prefill_finalize_kernel(FinalizeArgs a
         return;
     }
     const uint2* src = a.buf + (size_t)row * a.cap;
-    if (cnt > 0)
-        batched_copy<FIN_NT, 8>(cnt, [&](int i) { return src[i]; }, [&](int i, uint2 e) {
-            fkey[cnt - 1 - i] = score_key(__uint_as_float(e.x));  // the buffer holds descending positions
-        });
-    __syncthreads();
+    // all loads issued before any is used (indices clamped, so always in
+    // bounds; items past the count are never read back)
+    uint2 e[SEG];
+#pragma unroll
+    for (int u = 0; u < SEG; ++u) e[u] = src[max(cnt - 1 - (tid + u * FIN_NT), 0)];
+    uint32_t key[SEG];
+    int pos[SEG];
+#pragma unroll
+    for (int u = 0; u < SEG; ++u) {
+        key[u] = score_key(__uint_as_float(e[u].x));
+        pos[u] = (int)e[u].y;
+    }
+    // every candidate is kept when there are exactly K of them
+    const bool all = cnt == K;
     uint32_t T = 0u;  // key of the K-th largest candidate
     int gt = cnt;     // candidates with a key above T
-    if (cnt > K)
-        T = block_select_adaptive<FIN_NT>(cnt, K, [&](int i, bool* ok) { *ok = true; return fkey[i]; }, sel, &gt);
+    if (!all) {
+        const auto each = [&](auto&& f) {
+#pragma unroll
+            for (int u = 0; u < SEG; ++u)
+                if (tid + u * FIN_NT < cnt) f(key[u]);
+        };
+        T = block_select_each<FIN_NT>(K, each, sel, &gt, true);
+    }
     const int need_ties = K - gt;
+    // Ordered output: selected are every key above T and the first need_ties
+    // keys equal to T in position order.  Counts of both kinds per (item,
+    // wave) group, scanned in candidate order, give each candidate's slot.
+#pragma unroll
+    for (int u = 0; u < SEG; ++u) {
+        const bool ok = tid + u * FIN_NT < cnt;
+        const uint64_t mg = ballot(ok && (all || key[u] > T));
+        const uint64_t mt = ballot(ok && !all && key[u] == T);
+        if (lane_id() == 0) {
+            gcnt[0][u * NW + w] = __popcll(mg);
+            gcnt[1][u * NW + w] = __popcll(mt);
+        }
+    }
+    __syncthreads();
+    if (w == 0) {
+        // exclusive scan of the NE group counts by the first wave
+        constexpr int PER = (NE + 63) / 64;
+        const int l = lane_id();
+        int cg[PER], ct[PER], sg = 0, st = 0;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int e = l * PER + j;
+            cg[j] = e < NE ? gcnt[0][e] : 0;
+            ct[j] = e < NE ? gcnt[1][e] : 0;
+            sg += cg[j];
+            st += ct[j];
+        }
+        int eg = wave_incl_scan(sg) - sg, et = wave_incl_scan(st) - st;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int e = l * PER + j;
+            if (e < NE) {
+                gcnt[0][e] = eg;
+                gcnt[1][e] = et;
+            }
+            eg += cg[j];
+            et += ct[j];
+        }
+    }
+    __syncthreads();
     int32_t* Srow = a.S + (size_t)row * a.topk;
     float* Ssrow = a.Ss ? a.Ss + (size_t)row * a.topk : nullptr;
-    // ordered output: each thread owns a contiguous run of the (ascending)
-    // candidates; one scan gives the slot of its first selected entry.  Ties
-    // with the K-th key are taken in position order until K are selected.
-    const int seg = (cnt + FIN_NT - 1) / FIN_NT;
-    const int b0 = min(tid * seg, cnt), b1 = min(b0 + seg, cnt);
-    // this thread's positions, loaded unconditionally (clamped) so that they
-    // are all in flight during the counting and the scan
-    constexpr int SEGMAX = (CAPMAX + FIN_NT - 1) / FIN_NT;
-    int mypos[SEGMAX];
 #pragma unroll
-    for (int u = 0; u < SEGMAX; ++u) mypos[u] = (int)src[max(cnt - 1 - min(b0 + u, cnt - 1), 0)].y;
-    int ngt = 0, ntie = 0;
-    for (int i = b0; i < b1; ++i) {
-        const uint32_t key = fkey[i];
-        ngt += key > T;
-        ntie += key == T;
-    }
-    int egt, etie, tgt, ttie;
-    block_scan_int2<FIN_NT>(ngt, ntie, &egt, &etie, &tgt, &ttie, sel.scratch);
-    int slot = egt + min(etie, need_ties);
-    int ties_before = etie;
-#pragma unroll
-    for (int u = 0; u < SEGMAX; ++u) {
-        const int i = b0 + u;
-        if (i >= b1) break;
-        const uint32_t key = fkey[i];
-        bool sel = key > T;
-        if (key == T) sel = ties_before++ < need_ties;
-        if (sel) {
-            Srow[slot] = mypos[u];
-            if (Ssrow) Ssrow[slot] = key_score(key);
-            ++slot;
+    for (int u = 0; u < SEG; ++u) {
+        if (u * FIN_NT >= cnt) break;
+        const bool ok = tid + u * FIN_NT < cnt;
+        const bool isg = ok && (all || key[u] > T);
+        const bool ist = ok && !all && key[u] == T;
+        const uint64_t mg = ballot(isg), mt = ballot(ist);
+        const int rg = gcnt[0][u * NW + w] + rank_below(mg);  // keys above T before this one
+        const int rt = gcnt[1][u * NW + w] + rank_below(mt);  // keys equal to T before this one
+        if (isg || (ist && rt < need_ties)) {
+            const int slot = rg + min(rt, need_ties);
+            Srow[slot] = pos[u];
+            if (Ssrow) Ssrow[slot] = key_score(key[u]);
         }
     }
     for (int i = K + tid; i < a.topk; i += FIN_NT) {

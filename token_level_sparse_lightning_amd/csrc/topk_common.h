@@ -21,10 +21,11 @@ __device__ __forceinline__ int radix_shift(int p) { return p == 0 ? 21 : (p == 1
 __device__ __forceinline__ uint32_t radix_mask(int p) { return p == 2 ? 0x3ffu : 0x7ffu; }
 
 // ---------------------------------------------------------------------------
-// need-th largest (1 <= need <= number of valid keys) of key_of(i, &valid),
-// i < cnt, over a workgroup of NT threads; key_of reads workgroup-visible
-// memory and is called up to three times per index.  Returns the key T and
-// *gt = number of valid keys above T.
+// need-th largest (1 <= need <= number of keys) of the keys a workgroup of NT
+// threads holds between them: each(f) calls f(key) for every key the calling
+// thread holds (every key held by exactly one thread; the keys may sit in
+// registers or in workgroup-visible memory) and is called up to five times.
+// Returns the key T and *gt = number of keys above T.
 //
 // One histogram pass over the keys' own span [lo, hi] (2048 bins of 2^s keys)
 // finds the bin holding the result; the few keys of that bin are then ranked
@@ -45,30 +46,21 @@ struct SelectSmem {
     uint32_t tsh;
 };
 
-template <int NT, class KeyFn>
-__device__ uint32_t block_select_adaptive(int cnt, int need, KeyFn key_of, SelectSmem& sm, int* gt_out,
-                                          bool exact = true) {
+template <int NT, class Each>
+__device__ uint32_t block_select_each(int need, Each each, SelectSmem& sm, int* gt_out, bool exact) {
     const int tid = threadIdx.x;
     uint32_t lo = 0xffffffffu, hi = 0u;
-    for (int i = tid; i < cnt; i += NT) {
-        bool ok;
-        const uint32_t k = key_of(i, &ok);
-        if (ok) {
-            lo = min(lo, k);
-            hi = max(hi, k);
-        }
-    }
+    each([&](uint32_t k) {
+        lo = min(lo, k);
+        hi = max(hi, k);
+    });
     block_minmax_u32<NT>(&lo, &hi, sm.scratch);
     const uint32_t span = hi - lo;
     const int s = span < 2048u ? 0 : (32 - __clz(span)) - 11;
     for (int i = tid; i < 2048; i += NT) sm.hist[i] = 0;
     if (tid == 0) sm.bcnt = 0;
     __syncthreads();
-    for (int i = tid; i < cnt; i += NT) {
-        bool ok;
-        const uint32_t k = key_of(i, &ok);
-        if (ok) atomicAdd(&sm.hist[(k - lo) >> s], 1u);
-    }
+    each([&](uint32_t k) { atomicAdd(&sm.hist[(k - lo) >> s], 1u); });
     __syncthreads();
     int above;
     const int d = block_find_bin<NT, 2048>(sm.hist, need, &above, sm.scratch);
@@ -83,11 +75,9 @@ __device__ uint32_t block_select_adaptive(int cnt, int need, KeyFn key_of, Selec
         T = edge;
         gt = above;
     } else if (nb <= SEL_BLMAX) {
-        for (int i = tid; i < cnt; i += NT) {
-            bool ok;
-            const uint32_t k = key_of(i, &ok);
-            if (ok && ((k - lo) >> s) == (uint32_t)d) sm.blist[atomicAdd(&sm.bcnt, 1)] = k;
-        }
+        each([&](uint32_t k) {
+            if (((k - lo) >> s) == (uint32_t)d) sm.blist[atomicAdd(&sm.bcnt, 1)] = k;
+        });
         __syncthreads();
         if (tid < nb) {
             const uint32_t kj = sm.blist[tid];
@@ -114,11 +104,9 @@ __device__ uint32_t block_select_adaptive(int cnt, int need, KeyFn key_of, Selec
             const uint32_t dm = radix_mask(p);
             for (int i = tid; i < 2048; i += NT) sm.hist[i] = 0;
             __syncthreads();
-            for (int i = tid; i < cnt; i += NT) {
-                bool ok;
-                const uint32_t k = key_of(i, &ok);
-                if (ok && (k & pmask) == prefix) atomicAdd(&sm.hist[(k >> sh) & dm], 1u);
-            }
+            each([&](uint32_t k) {
+                if ((k & pmask) == prefix) atomicAdd(&sm.hist[(k >> sh) & dm], 1u);
+            });
             __syncthreads();
             int ab;
             const int dd = block_find_bin<NT, 2048>(sm.hist, left, &ab, sm.scratch);
@@ -132,6 +120,21 @@ __device__ uint32_t block_select_adaptive(int cnt, int need, KeyFn key_of, Selec
     __syncthreads();
     *gt_out = gt;
     return T;
+}
+
+// Keys in workgroup-visible memory: key_of(i, &valid) for i < cnt, read by
+// thread i % NT.
+template <int NT, class KeyFn>
+__device__ uint32_t block_select_adaptive(int cnt, int need, KeyFn key_of, SelectSmem& sm, int* gt_out,
+                                          bool exact = true) {
+    const auto each = [&](auto&& f) {
+        for (int i = threadIdx.x; i < cnt; i += NT) {
+            bool ok;
+            const uint32_t k = key_of(i, &ok);
+            if (ok) f(k);
+        }
+    };
+    return block_select_each<NT>(need, each, sm, gt_out, exact);
 }
 
 // Exact selection of the K = min(k, L) best of sc[0..L) ordered by (score desc,
