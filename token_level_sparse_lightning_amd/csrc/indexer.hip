@@ -507,7 +507,7 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
 // ---------------------------------------------------------------------------
 // Stage 2: exact selection from a row's candidate buffer.
 // ---------------------------------------------------------------------------
-constexpr int FIN_NT = 512;
+constexpr int FIN_NT = 256;  // four waves per row: more rows in flight per CU than with eight
 
 struct FinalizeArgs {
     const uint2* buf;
