@@ -22,8 +22,8 @@
 
 namespace tlsl {
 
-constexpr int TT_NT = 1024;             // threshold workgroup
-constexpr int TT_SAMPLE_MAX = 8192;     // sample values held in LDS
+constexpr int TT_NT = 256;              // threshold workgroup
+constexpr int TT_SAMPLE_MAX = 8192;     // sample values per row (held in registers)
 constexpr int TF_NT = 256;              // filter workgroup
 constexpr int TF_PER = 16;              // scores per filter thread
 constexpr int TF_CHUNK = TF_NT * TF_PER;
@@ -68,7 +68,8 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, int* scratch) 
 __device__ __forceinline__ int sample_stride(int L) { return max(16, (L + TT_SAMPLE_MAX - 1) / TT_SAMPLE_MAX); }
 
 __global__ __launch_bounds__(TT_NT) void topk_threshold_kernel(TopkArgs a) {
-    __shared__ uint32_t skeys[TT_SAMPLE_MAX];
+    // sample j of the row is held in registers by thread j % TT_NT
+    constexpr int SEG = TT_SAMPLE_MAX / TT_NT;
     __shared__ SelectSmem sel;
     const int r = blockIdx.x, tid = threadIdx.x;
     const int L = max(a.row_len[r], 0);
@@ -83,12 +84,21 @@ __global__ __launch_bounds__(TT_NT) void topk_threshold_kernel(TopkArgs a) {
         return;
     }
     const float* sc = a.scores + a.row_start[r];
-    batched_copy<TT_NT, 16>(ns, [&](int j) { return sc[(size_t)j * stride]; },
-                            [&](int j, float v) { skeys[j] = score_key(v); });
-    __syncthreads();
+    // every load issued before any is used (indices clamped, so always in
+    // bounds; samples past ns are never visited)
+    float v[SEG];
+#pragma unroll
+    for (int u = 0; u < SEG; ++u) v[u] = sc[(size_t)min(tid + u * TT_NT, ns - 1) * stride];
+    uint32_t key[SEG];
+#pragma unroll
+    for (int u = 0; u < SEG; ++u) key[u] = score_key(v[u]);
+    const auto each = [&](auto&& f) {
+#pragma unroll
+        for (int u = 0; u < SEG; ++u)
+            if (tid + u * TT_NT < ns) f(key[u]);
+    };
     int gt;
-    const uint32_t T = block_select_adaptive<TT_NT>(ns, need, [&](int i, bool* ok) { *ok = true; return skeys[i]; },
-                                                    sel, &gt);
+    const uint32_t T = block_select_each<TT_NT>(need, each, sel, &gt, true);
     if (tid == 0) a.theta[r] = key_score(T);
 }
 
