@@ -10,6 +10,8 @@ rows of the path measured on their own workloads:
   prefill_long  index_prefill, n=131072, fp8                       (--long)
   attn_prefill  sparse_attn_prefill over that selection, n=32768,
                 H=128, Dqk=576, Dv=512, bf16
+  attn_dense    dense_attn_prefill (short prefill: n <= k, every query over
+                all of its history), n=2048, same heads and dims
   decode        one decode step of 64 ragged sequences (L ~ U[16384,131072]):
                 index_decode + topk_select + sparse_attn_decode, tokens/s
 
@@ -169,6 +171,27 @@ def bench_attn_prefill(S, n, seed, steps, warmup):
     del q, kv, out
     return dict(workload=f"sparse attention prefill: n={n}, H={H}, Dqk={Dqk}, Dv={Dv}, k=2048, bf16",
                 valid_slots=valid, flops_per_call=flops, kernel="sparse_attn_kernel", kernel_tflops=ach,
+                peak_tflops=PEAK_BF16_TFLOPS, frac=ach / PEAK_BF16_TFLOPS, **tm.as_dict())
+
+
+def bench_attn_dense(n, seed, steps, warmup):
+    H, Dqk, Dv = 128, 576, 512
+    log(f"dense attn prefill n={n}: generating inputs")
+    q, kv = synth.attn_prefill(1, n, H, Dqk, synth.DT_BF16, seed, device=DEV)
+    out = torch.empty((1, n, H, Dv), dtype=torch.bfloat16, device=DEV)
+    scale = 1.0 / math.sqrt(Dqk)
+
+    def call():
+        tl.dense_attn_prefill(q, kv, scale, Dv, out=out)
+
+    tm = time_calls(call, steps, warmup, kernel="sparse_attn_kernel")
+    pairs = n * (n + 1) // 2
+    flops = 2.0 * H * (Dqk + Dv) * pairs
+    ach = flops / (tm.kernel_avg * 1e-3) / 1e12
+    log(f"dense attn prefill: {tm.ev_med:.3f} ms/call (events, median), {ach:.1f} TFLOP/s")
+    del q, kv, out
+    return dict(workload=f"dense (short) attention prefill: n={n}, H={H}, Dqk={Dqk}, Dv={Dv}, bf16",
+                causal_pairs=pairs, flops_per_call=flops, kernel="sparse_attn_kernel", kernel_tflops=ach,
                 peak_tflops=PEAK_BF16_TFLOPS, frac=ach / PEAK_BF16_TFLOPS, **tm.as_dict())
 
 
@@ -363,7 +386,7 @@ def main():
     ap.add_argument("--long", action="store_true", help="also time the n=131072 prefill")
     ap.add_argument("--quick", action="store_true", help="headline workload (and calibration) only")
     ap.add_argument("--only", default="", help="comma list of extra workloads to run: "
-                    "prefill_fp8,attn_prefill,decode,prefill_long (default: all but prefill_long)")
+                    "prefill_fp8,attn_prefill,attn_dense,decode,prefill_long (default: all but prefill_long)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-calib", action="store_true", help="skip the copy and matrix-core calibration")
     args = ap.parse_args()
@@ -382,7 +405,7 @@ def main():
     del S
     torch.cuda.empty_cache()
     extra = {}
-    want = set(args.only.split(",")) if args.only else {"prefill_fp8", "attn_prefill", "decode"}
+    want = set(args.only.split(",")) if args.only else {"prefill_fp8", "attn_prefill", "attn_dense", "decode"}
     if args.long:
         want.add("prefill_long")
     if not args.quick:
@@ -392,6 +415,9 @@ def main():
             if "attn_prefill" in want:
                 extra["attn_prefill"] = bench_attn_prefill(S3, 32768, args.seed + 1, max(3, args.steps // 4), 1)
             del S3
+            torch.cuda.empty_cache()
+        if "attn_dense" in want:
+            extra["attn_dense"] = bench_attn_dense(2048, args.seed + 2, max(5, args.steps // 2), 2)
             torch.cuda.empty_cache()
         if "decode" in want:
             extra["decode"] = bench_decode(args.seed + 3, args.steps, args.warmup)

@@ -24,7 +24,8 @@
  *    otherwise *ws_bytes must hold the size of `workspace`, at least the
  *    queried size.  A workspace may be reused once the call that used it has
  *    completed on its stream; calls that overlap must not share one.
- *    index_decode and sparse_attn_prefill need no workspace:
+ *    index_decode, sparse_attn_prefill and dense_attn_prefill need no
+ *    workspace:
  *    their workspace argument is ignored, and *ws_bytes (if ws_bytes is not
  *    NULL) receives 0.
  *  - Arguments are validated on the host before anything is launched; a
@@ -153,6 +154,26 @@ int topk_select(const float* scores, const int64_t* row_start, const int32_t* ro
 int sparse_attn_prefill(const void* q, const void* kv, const int32_t* S, int B, int n, int H,
                         int Dqk, int Dv, int k, float softmax_scale, tlsl_dtype dt, void* out,
                         float* lse, void* workspace, size_t* ws_bytes, hipStream_t stream);
+
+/*
+ * dense_attn_prefill -- the short-prefill path: causal attention of every
+ * query over all of its history.  When t + 1 <= k, TopK(min(k, t+1)) of the
+ * DSA page, section 1.1 eq.(2) keeps every position 0..t, so eq.(3) over S_t
+ * is plain masked attention; section 2 (the paragraph on short prefill) notes
+ * that for short sequences the top-k, index materialisation and gather cost
+ * more than the attention they save, and that serving picks the path by
+ * length.  A caller with n <= k therefore skips index_prefill and calls this.
+ * The result equals sparse_attn_prefill with k = n and S[b,t,i] = i for
+ * i <= t (-1 above), bit for bit.
+ *
+ *   q   [B,n,H,Dqk] dtype dt,  kv [B,n,Dqk] dtype dt
+ *   out [B,n,H,Dv] dtype dt,   lse [B,n,H] fp32 (optional)
+ * Supported shapes as sparse_attn_prefill, with 1 <= n <= 4096 (longer
+ * sequences: TLSL_ERR_UNSUPPORTED).
+ */
+int dense_attn_prefill(const void* q, const void* kv, int B, int n, int H, int Dqk, int Dv,
+                       float softmax_scale, tlsl_dtype dt, void* out, float* lse,
+                       void* workspace, size_t* ws_bytes, hipStream_t stream);
 
 /*
  * sparse_attn_decode -- as sparse_attn_prefill for the newest token of each

@@ -169,6 +169,23 @@ int ora_topk_rows(const float *scores, const int64_t *row_start, const int32_t *
     return 0;
 }
 
+/* every listed row (sequence) must name one of the batch's rows */
+static int rows_ok(const int64_t *rows, int nrows, int64_t limit)
+{
+    for (int r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= limit)
+            return 0;
+    return 1;
+}
+
+static int seqs_ok(const int32_t *seqs, int nseq, int B)
+{
+    for (int i = 0; i < nseq; ++i)
+        if (seqs[i] < 0 || seqs[i] >= B)
+            return 0;
+    return 1;
+}
+
 /* Prefill: for each requested flattened row (b*n + t) compute I[t, 0..t]
  * (eq.1), select (eq.2).  Optional per-row outputs of width n: the fp32 scores
  * and magnitude sums of the causal part (entries beyond t are left as NaN). */
@@ -180,6 +197,8 @@ int ora_index_prefill_rows(int dt, const void *qI, const float *q_scale, const v
     if (!qI || !kI || !wI || !rows || !S || B <= 0 || n <= 0 || HI <= 0 || DI <= 0 || k <= 0)
         return -1;
     if (dt == ORA_FP8 && (!q_scale || !k_scale))
+        return -1;
+    if (!rows_ok(rows, nrows, (int64_t)B * n))
         return -1;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int r = 0; r < nrows; ++r) {
@@ -227,6 +246,8 @@ int ora_index_decode(int dt, const void *qI, const float *q_scale, const void *k
     if (!qI || !kI || !wI || !cu || !seqs || !scores || B <= 0 || HI <= 0 || DI <= 0)
         return -1;
     if (dt == ORA_FP8 && (!q_scale || !k_scale))
+        return -1;
+    if (!seqs_ok(seqs, nseq, B))
         return -1;
     for (int i = 0; i < nseq; ++i) {
         int b = seqs[i];
@@ -324,6 +345,8 @@ int ora_sparse_attn_prefill_rows(int dt, const void *q, const void *kv, const in
         return -1;
     if (dt == ORA_FP8)
         return -1;
+    if (!rows_ok(rows, nrows, (int64_t)B * n))
+        return -1;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int r = 0; r < nrows; ++r) {
         int64_t row = rows[r];
@@ -345,6 +368,8 @@ int ora_sparse_attn_decode(int dt, const void *q, const void *kv, const int64_t 
     if (!q || !kv || !cu || !S || !seqs || !out || B <= 0 || H <= 0 || Dv > Dqk || k <= 0)
         return -1;
     if (dt == ORA_FP8)
+        return -1;
+    if (!seqs_ok(seqs, nseq, B))
         return -1;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int i = 0; i < nseq; ++i) {

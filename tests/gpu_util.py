@@ -29,4 +29,4 @@ def sample_rows(n, k, count, seed=0, extra=()):
     base |= {int(e) for e in extra if 0 <= e < n}
     rng = np.random.default_rng(seed)
     rest = rng.choice(n, size=min(n, count), replace=False)
-    return np.array(sorted({int(x) for x in base if x >= 0} | {int(x) for x in rest}), dtype=np.int64)
+    return np.array(sorted({int(x) for x in base if 0 <= x < n} | {int(x) for x in rest}), dtype=np.int64)

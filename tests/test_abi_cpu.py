@@ -161,7 +161,21 @@ def test_attention_validation():
     assert call(k=4097) == ERR_UNSUP                                # one workgroup stages at most 4096 slots
     assert call(sc=0.0) == ERR_SHAPE
     assert call(sc=float("nan")) == ERR_SHAPE
+    assert call(sc=float("inf")) == ERR_SHAPE
     assert call(out=MIS) == ERR_ALIGN
+    d = lib.dense_attn_prefill
+
+    def dcall(**kw):
+        a = args(**kw)
+        return d(a["q"], a["kv"], a["B"], a["n"], a["H"], a["Dqk"], a["Dv"], a["sc"], a["dt"], a["out"], None,
+                 None, ctypes.byref(s), None)
+
+    assert dcall(kv=None) == ERR_NULL
+    assert dcall(B=0) == ERR_SHAPE
+    assert dcall(n=4097) == ERR_UNSUP                               # every row's history fits one workgroup
+    assert dcall(H=17, Dqk=80, Dv=64, dt=0) == ERR_UNSUP
+    assert dcall(sc=float("inf")) == ERR_SHAPE
+    assert dcall(q=MIS) == ERR_ALIGN
     g = lib.sparse_attn_decode
     size = _ws()
     assert g(P, P, P, P, 64, 128, 576, 512, 2048, 0.04, 1, P, None, None, ctypes.byref(size), None) == OK

@@ -290,6 +290,55 @@ def test_sparse_attn_prefill_empty_rows():
     np.testing.assert_array_equal(o[5], np.repeat(kv[0, 2:3, :512].float().numpy(), H, 0))
 
 
+# ---------------------------------------------------------------------------
+# dense_attn_prefill (short prefill, n <= k)
+# ---------------------------------------------------------------------------
+def _all_history(B, n):
+    """What TopK(min(k, t+1)) keeps when t+1 <= k: every position 0..t."""
+    S = np.full((B, n, n), -1, np.int32)
+    for t in range(n):
+        S[:, t, : t + 1] = np.arange(t + 1, dtype=np.int32)
+    return S
+
+
+@pytest.mark.parametrize("dt,B,H,Dqk,Dv,n", [(F32, 2, 4, 80, 64, 300), (BF16, 1, 128, 576, 512, 200),
+                                             (BF16, 2, 16, 576, 512, 1000), (BF16, 1, 8, 576, 512, 4096),
+                                             (BF16, 1, 100, 576, 512, 1)])
+def test_dense_attn_prefill(dt, B, H, Dqk, Dv, n):
+    q, kv = synth.attn_prefill(B, n, H, Dqk, dt, seed=15)
+    scale = 1.0 / math.sqrt(Dqk)
+    announce(f"dense_attn_prefill dt={dt} B={B} H={H} n={n}")
+    out, lse = tl.dense_attn_prefill(to_dev(q), to_dev(kv), scale, Dv, want_lse=True)
+    torch.cuda.synchronize()
+    # rows around the 32-slot tiles and both ends of every batch row
+    per = sample_rows(n, 32, 12, seed=n, extra=(31, 33, 63, 64, 65))
+    rows = np.unique(np.concatenate([b * n + per for b in range(B)]))
+    ref, ref_lse = oracle.sparse_attn_prefill_rows(dt, host(q), host(kv), _all_history(B, n), scale, rows, Dv)
+    got = out.float().cpu().numpy().reshape(B * n, H, Dv)[rows]
+    tol = parity.ATTN_ATOL_F32 if dt == F32 else parity.ATTN_ATOL_BF16
+    err = np.abs(got - ref).max()
+    assert err <= tol, err
+    np.testing.assert_allclose(lse.cpu().numpy().reshape(B * n, H)[rows], ref_lse, rtol=1e-4, atol=1e-4)
+
+
+def test_short_prefill_path_equals_selected_path():
+    """With k >= n the indexer keeps every position, and the dense path gives
+    the sparse path's result over that selection bit for bit."""
+    n, H = 333, 32
+    ix = synth.indexer_prefill(1, n, 16, 64, BF16, seed=16, device=DEV)
+    announce("short prefill: index_prefill k=n, sparse vs dense attention")
+    S, _ = tl.index_prefill(ix.q, ix.k, ix.w, n, q_scale=ix.q_scale, k_scale=ix.k_scale)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(S.cpu().numpy(), _all_history(1, n))
+    q, kv = synth.attn_prefill(1, n, H, 576, BF16, seed=17)
+    qd, kvd = to_dev(q), to_dev(kv)
+    o_s, l_s = tl.sparse_attn_prefill(qd, kvd, S, 0.05, 512, want_lse=True)
+    o_d, l_d = tl.dense_attn_prefill(qd, kvd, 0.05, 512, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_d)
+    assert torch.equal(l_s, l_d)
+
+
 @pytest.mark.parametrize("dt,H,Dqk,Dv", [(BF16, 128, 576, 512), (F32, 4, 80, 64)])
 def test_sparse_attn_decode(dt, H, Dqk, Dv):
     lengths = [1, 0, 5, 64, 2048, 3000, 5000]  # an empty sequence: zero output, lse -inf

@@ -327,3 +327,21 @@ def test_decode_attention_equals_prefill_row():
     outd, lsed = oracle.sparse_attn_decode(0, qd, kvc, cu, Sd, 0.5, Dv)
     np.testing.assert_array_equal(outd, out[ts])
     np.testing.assert_array_equal(lsed, lse[ts])
+
+
+def test_oracle_refuses_rows_outside_the_batch():
+    """A listed row or sequence outside the batch is an error, not a read past the inputs."""
+    q = np.zeros((1, 4, 2, 80), np.float32)
+    kv = np.zeros((1, 4, 80), np.float32)
+    S = np.zeros((1, 4, 4), np.int32)
+    for rows in ([4], [-1]):
+        with pytest.raises(ValueError):
+            oracle.sparse_attn_prefill_rows(0, q, kv, S, 0.1, np.array(rows), 64)
+    qi = np.zeros((1, 4, 4, 32), np.float32)
+    ki = np.zeros((1, 4, 32), np.float32)
+    wi = np.zeros((1, 4, 4), np.float32)
+    with pytest.raises(ValueError):
+        oracle.index_prefill_rows(0, qi, None, ki, None, wi, 2, np.array([0, 4]))
+    cu = np.array([0, 4], np.int64)
+    with pytest.raises(ValueError):
+        oracle.sparse_attn_decode(0, q[:, 0], kv[0], cu, S[:, 0], 0.1, 64, seqs=np.array([1]))

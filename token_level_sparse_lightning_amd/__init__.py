@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     TlslError,
     calib_copy,
     calib_mfma,
+    dense_attn_prefill,
     index_decode,
     index_prefill,
     index_prefill_workspace_bytes,

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libtlsl.so")
 F32, BF16, FP8_E4M3 = 0, 1, 2
 
 EXPORTS = ("index_prefill", "index_decode", "topk_select", "sparse_attn_prefill",
-           "sparse_attn_decode", "tlsl_last_error", "tlsl_version",
+           "dense_attn_prefill", "sparse_attn_decode", "tlsl_last_error", "tlsl_version",
            # measurement aids (include/tlsl_measure.h)
            "tlsl_timer_arm", "tlsl_timer_collect", "tlsl_calib_copy", "tlsl_calib_mfma")
 
@@ -46,8 +46,10 @@ def load():
     lib.index_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, SZ, P]
     lib.topk_select.argtypes = [P, P, P, I, I, I, P, P, P, SZ, P]
     lib.sparse_attn_prefill.argtypes = [P, P, P, I, I, I, I, I, I, F, I, P, P, P, SZ, P]
+    lib.dense_attn_prefill.argtypes = [P, P, I, I, I, I, I, F, I, P, P, P, SZ, P]
     lib.sparse_attn_decode.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, P, P, SZ, P]
-    for fn in ("index_prefill", "index_decode", "topk_select", "sparse_attn_prefill", "sparse_attn_decode"):
+    for fn in ("index_prefill", "index_decode", "topk_select", "sparse_attn_prefill", "dense_attn_prefill",
+               "sparse_attn_decode"):
         getattr(lib, fn).restype = I
     lib.tlsl_last_error.restype = ctypes.c_char_p
     lib.tlsl_version.restype = ctypes.c_char_p
@@ -186,6 +188,20 @@ def sparse_attn_prefill(q, kv, S, softmax_scale, Dv, out=None, lse=None, want_ls
                                  float(softmax_scale), dtype_code(q), _ptr(out), _ptr(lse), None,
                                  None, _stream(stream))
     _check("sparse_attn_prefill", rc)
+    return out, lse
+
+
+def dense_attn_prefill(q, kv, softmax_scale, Dv, out=None, lse=None, want_lse=False, stream=None):
+    """Causal attention over all history (short prefill, n <= k): (out [B,n,H,Dv], lse or None)."""
+    lib = load()
+    B, n, H, Dqk = q.shape
+    if out is None:
+        out = torch.empty((B, n, H, Dv), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, n, H), dtype=torch.float32, device=q.device)
+    rc = lib.dense_attn_prefill(_ptr(q), _ptr(kv), B, n, H, Dqk, Dv, float(softmax_scale),
+                                dtype_code(q), _ptr(out), _ptr(lse), None, None, _stream(stream))
+    _check("dense_attn_prefill", rc)
     return out, lse
 
 

@@ -1,6 +1,7 @@
 // abi.cpp -- the extern "C" entry points declared in include/tlsl.h: argument
 // validation (all of it on the host, before anything is launched), workspace
 // sizing and dispatch to the gfx950 kernels.  No exception crosses the ABI.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -157,7 +158,7 @@ int sparse_attn_prefill(const void* q, const void* kv, const int32_t* S, int B, 
     if (!tlsl::attn_supported(s))
         return fail(TLSL_ERR_UNSUPPORTED, "sparse_attn_prefill: (dtype %s, H=%d, Dqk=%d, Dv=%d) not built "
                     "(bf16: Dqk 576, Dv 512, H<=128; f32: Dqk 80, Dv 64, H<=16)", dt_name(dt), H, Dqk, Dv);
-    if (!(softmax_scale > 0.f) || softmax_scale != softmax_scale)
+    if (!(softmax_scale > 0.f) || !isfinite(softmax_scale))
         return fail(TLSL_ERR_SHAPE, "sparse_attn_prefill: softmax_scale must be positive and finite");
     if (!aligned16(q) || !aligned16(kv) || !aligned16(S) || !aligned16(out) || !aligned16(lse))
         return fail(TLSL_ERR_ALIGN, "sparse_attn_prefill: pointers not 16-byte aligned");
@@ -165,6 +166,28 @@ int sparse_attn_prefill(const void* q, const void* kv, const int32_t* S, int B, 
     if (ws_bytes) *ws_bytes = 0;  // needs no workspace
     return launch_result(tlsl::launch_sparse_attn_prefill(s, q, kv, S, B, n, k, softmax_scale, out, lse, stream),
                          "sparse_attn_prefill");
+}
+
+int dense_attn_prefill(const void* q, const void* kv, int B, int n, int H, int Dqk, int Dv, float softmax_scale,
+                       tlsl_dtype dt, void* out, float* lse, void* workspace, size_t* ws_bytes, hipStream_t stream) {
+    if (!q || !kv || !out) return fail(TLSL_ERR_NULL, "dense_attn_prefill: NULL pointer argument");
+    if (B <= 0 || n <= 0 || H <= 0) return fail(TLSL_ERR_SHAPE, "dense_attn_prefill: B, n and H must be positive");
+    if ((int64_t)B * n > (int64_t)1 << 30) return fail(TLSL_ERR_SHAPE, "dense_attn_prefill: B*n too large");
+    if (n > 4096) return fail(TLSL_ERR_UNSUPPORTED, "dense_attn_prefill: n=%d above the supported 4096", n);
+    if (dt != TLSL_F32 && dt != TLSL_BF16) return fail(TLSL_ERR_UNSUPPORTED, "dense_attn_prefill: dtype %d not supported", dt);
+    tlsl::AttnShape s{dt, H, Dqk, Dv};
+    if (!tlsl::attn_supported(s))
+        return fail(TLSL_ERR_UNSUPPORTED, "dense_attn_prefill: (dtype %s, H=%d, Dqk=%d, Dv=%d) not built "
+                    "(bf16: Dqk 576, Dv 512, H<=128; f32: Dqk 80, Dv 64, H<=16)", dt_name(dt), H, Dqk, Dv);
+    if (!(softmax_scale > 0.f) || !isfinite(softmax_scale))
+        return fail(TLSL_ERR_SHAPE, "dense_attn_prefill: softmax_scale must be positive and finite");
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || !aligned16(lse))
+        return fail(TLSL_ERR_ALIGN, "dense_attn_prefill: pointers not 16-byte aligned");
+    (void)workspace;
+    if (ws_bytes) *ws_bytes = 0;  // needs no workspace
+    // the sparse kernel with n slots per row and no index array: slot i is position i
+    return launch_result(tlsl::launch_sparse_attn_prefill(s, q, kv, nullptr, B, n, n, softmax_scale, out, lse, stream),
+                         "dense_attn_prefill");
 }
 
 int sparse_attn_decode(const void* q, const void* kv_cache, const int64_t* cu_seqlens, const int32_t* S, int B, int H,
@@ -177,7 +200,7 @@ int sparse_attn_decode(const void* q, const void* kv_cache, const int64_t* cu_se
     tlsl::AttnShape s{dt, H, Dqk, Dv};
     if (!tlsl::attn_supported(s))
         return fail(TLSL_ERR_UNSUPPORTED, "sparse_attn_decode: (dtype %s, H=%d, Dqk=%d, Dv=%d) not built", dt_name(dt), H, Dqk, Dv);
-    if (!(softmax_scale > 0.f) || softmax_scale != softmax_scale)
+    if (!(softmax_scale > 0.f) || !isfinite(softmax_scale))
         return fail(TLSL_ERR_SHAPE, "sparse_attn_decode: softmax_scale must be positive and finite");
     if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(S) || !aligned16(out) || !aligned16(lse) || !aligned16(cu_seqlens))
         return fail(TLSL_ERR_ALIGN, "sparse_attn_decode: pointers not 16-byte aligned");

@@ -49,7 +49,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return (uint16_t)
 struct AttnArgs {
     const unsigned char* q;   // [rows][H][Dqk]
     const unsigned char* kv;  // entries [.][Dqk]
-    const int32_t* S;         // [rows][k]
+    const int32_t* S;         // [rows][k]; NULL: slot i of every row is position i (dense prefill)
     const int64_t* cu;        // decode: [B+1]; prefill: null
     int n;                    // prefill sequence length (rows = B*n)
     int H, k, nsplit;
@@ -149,12 +149,13 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     const int send = min(a.k, sbeg + per);
     const int nsl = max(send - sbeg, 0);
     const int ntiles = (nsl + AT_TS - 1) / AT_TS;
-    const int32_t* Srow = a.S + (size_t)qrow * a.k;
+    // no S (dense prefill): slot i is position i
+    const int32_t* Srow = a.S ? a.S + (size_t)qrow * a.k : nullptr;
 
     // the row's slot range, staged once: valid position or -1, padded to whole
     // tiles; tiles without a valid slot are skipped
     for (int i = tid; i < ntiles * AT_TS; i += NT) {
-        const int pos = i < nsl ? Srow[sbeg + i] : -1;
+        const int pos = i < nsl ? (Srow ? Srow[sbeg + i] : sbeg + i) : -1;
         slots[i] = (pos >= 0 && pos <= limit) ? pos : -1;
     }
     for (int i = tid; i < ntiles; i += NT) tile_any[i] = 0;
