@@ -138,7 +138,9 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
         kv_base = a.cu[qrow];
         limit = (int)(a.cu[qrow + 1] - kv_base) - 1;
     } else {
-        qrow = rs;
+        // latest rows first: the rows with the longest histories start early
+        // and the short ones fill the tail
+        qrow = a.rows - 1 - rs;
         split = 0;
         const int b = qrow / a.n;
         kv_base = (int64_t)b * a.n;
