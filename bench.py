@@ -353,8 +353,8 @@ TRAFFIC_SOURCES = ("indexer.hip", "tlsl_device.h", "tlsl_internal.h", "topk_comm
 TRAFFIC = {
     # profiles/prefill_score_kernel_bf16_n8192.md
     "prefill_score_kernel": {
-        "sources_sha256": "8c03ea05c6a6787667b9d20ab65d20801fe71e1dd39da3a87cc621f7cd686e8e",
-        "fetch_kib": 85341.2656, "write_kib": 168479.4141,
+        "sources_sha256": "e6f1b48c17e95d024acb1ab248b008b5ba3dfd3d24e7f7c2e52e5b3f806d360a",
+        "fetch_kib": 85347.625, "write_kib": 168479.1562,
         "copy_fetch_kib": 524302.0982, "copy_write_kib": 1048576.0, "copy_bytes": 1 << 30,
     },
 }
