@@ -56,7 +56,7 @@ def _score_rows(seed):
     return flat, starts, np.array([len(r) for r in rows], np.int32)
 
 
-@pytest.mark.parametrize("k", [1, 64, 2048])
+@pytest.mark.parametrize("k", [1, 64, 2048, 4096])
 def test_topk_select_exact(k):
     flat, starts, lens = _score_rows(k)
     announce(f"topk_select k={k} rows={len(lens)}")
@@ -123,7 +123,7 @@ def test_index_prefill_dyadic_exact(B, n, HI, DI, k):
 
 
 @pytest.mark.parametrize("dt,n,k", [(BF16, 3000, 256), (FP8, 3000, 256), (BF16, 2500, 2048),
-                                    (FP8, 6000, 2048)])
+                                    (FP8, 6000, 2048), (BF16, 9000, 4096), (FP8, 7000, 3000)])
 def test_index_prefill_lowp(dt, n, k):
     HI, DI = 64, 128
     inp = synth.indexer_prefill(1, n, HI, DI, dt, seed=2, planted=True)
@@ -133,7 +133,7 @@ def test_index_prefill_lowp(dt, n, k):
     for t in range(n):
         msg = parity.check_structure(S[t], t, k)
         assert msg is None, (t, msg)
-    rows = sample_rows(n, k, 40, seed=dt, extra=[255, 767, 768, 4351, 4352])
+    rows = sample_rows(n, k, 40, seed=dt, extra=[255, 767, 768, 4351, 4352, 8447, 8448])
     S_o, _, sc, mg = _oracle_rows(inp, k, rows)
     rep = parity.check_selection(S[rows], S_o, rows, k, sc)
     assert rep.ok(), rep.summary()
