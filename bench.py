@@ -353,7 +353,7 @@ TRAFFIC_SOURCES = ("indexer.hip", "tlsl_device.h", "tlsl_internal.h", "topk_comm
 TRAFFIC = {
     # profiles/prefill_score_kernel_bf16_n8192.md
     "prefill_score_kernel": {
-        "sources_sha256": "e6f1b48c17e95d024acb1ab248b008b5ba3dfd3d24e7f7c2e52e5b3f806d360a",
+        "sources_sha256": "848709082d78f13485d39216b597162e4cf04d8960f2fd8cd033ca121fb9af4d",
         "fetch_kib": 85347.625, "write_kib": 168479.1562,
         "copy_fetch_kib": 524302.0982, "copy_write_kib": 1048576.0, "copy_bytes": 1 << 30,
     },

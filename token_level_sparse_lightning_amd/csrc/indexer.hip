@@ -14,8 +14,9 @@
 //     threshold.  It then walks all causal key tiles from the diagonal down,
 //     appends every (score, position) that reaches the threshold to the
 //     query's candidate buffer (descending position order) and counts them.
-//  2. prefill_finalize: one workgroup per row selects the exact top-k from the
-//     buffer (radix select in LDS) and writes S in ascending position order.
+//  2. prefill_finalize: one workgroup per row reads the buffer once into
+//     registers, selects the exact top-k (histogram select over the
+//     register-held keys) and writes S in ascending position order.
 //     A row whose buffer missed (fewer candidates than min(k, t+1): the sample
 //     threshold overshot) or overflowed goes on a fallback list.
 //  3. prefill_fallback: rescores the listed rows in full (spread over the
