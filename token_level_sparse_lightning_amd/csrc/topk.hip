@@ -25,7 +25,7 @@ namespace tlsl {
 constexpr int TT_NT = 256;              // threshold workgroup
 constexpr int TT_SAMPLE_MAX = 8192;     // sample values per row (held in registers)
 constexpr int TF_NT = 256;              // filter workgroup
-constexpr int TF_PER = 16;              // scores per filter thread
+constexpr int TF_PER = 8;               // scores per filter thread (more workgroups in flight than with 16)
 constexpr int TF_CHUNK = TF_NT * TF_PER;
 constexpr int TFIN_NT = 1024;           // final workgroup
 constexpr int TSEL_CAPMAX = 8448;       // candidate buffer entries per row, max
