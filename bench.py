@@ -354,8 +354,8 @@ TRAFFIC = {
     # profiles/prefill_score_kernel_bf16_n8192.md
     "prefill_score_kernel": {
         "sources_sha256": "848709082d78f13485d39216b597162e4cf04d8960f2fd8cd033ca121fb9af4d",
-        "fetch_kib": 85347.625, "write_kib": 168479.1562,
-        "copy_fetch_kib": 524302.0982, "copy_write_kib": 1048576.0, "copy_bytes": 1 << 30,
+        "fetch_kib": 85372.9062, "write_kib": 168480.1562,
+        "copy_fetch_kib": 524302.1429, "copy_write_kib": 1048576.0, "copy_bytes": 1 << 30,
     },
 }
 
