@@ -1,19 +1,24 @@
 """Benchmark of the DSA token-selection path on one MI355X.
 
 Prints ONE JSON line.  The headline is the prefill Lightning Indexer + causal
-top-k (index_prefill) on B=1, n=8192, H^I=64, d^I=128, k=2048, bf16 inputs
-with planted keys; its metric is causal query-key pairs per second (a pair is
-(t, s) with s <= t; B*n*(n+1)/2 per call).  The same line carries the other
-rows of the path measured on their own workloads:
+top-k (index_prefill) on the largest single-GPU configuration: B=1, n=131072,
+H^I=64, d^I=128, k=2048, fp8 e4m3 with per-token scales, planted keys at
+distances up to 100,000.  Its metric is causal query-key pairs per second (a
+pair is (t, s) with s <= t; B*n*(n+1)/2 per call).  The same line carries the
+other rows of the path, each on its own workload (``extra``):
 
-  prefill_fp8   index_prefill, n=32768, fp8 e4m3 with per-token scales
-  prefill_long  index_prefill, n=131072, fp8                       (--long)
-  attn_prefill  sparse_attn_prefill over that selection, n=32768,
-                H=128, Dqk=576, Dv=512, bf16
-  attn_dense    dense_attn_prefill (short prefill: n <= k, every query over
-                all of its history), n=2048, same heads and dims
-  decode        one decode step of 64 ragged sequences (L ~ U[16384,131072]):
-                index_decode + topk_select + sparse_attn_decode, tokens/s
+  attn_prefill_131072  sparse_attn_prefill over the headline's selection,
+                       n=131072, H=128, Dqk=576, Dv=512, bf16
+  prefill_bf16_8192    index_prefill, n=8192, bf16
+  prefill_fp8_32768    index_prefill, n=32768, fp8
+  attn_prefill_32768   sparse_attn_prefill over that selection
+  attn_dense_2048      dense_attn_prefill (short prefill: n <= k, every query
+                       over all of its history), n=2048, H=128
+  decode               one decode step of 64 ragged sequences
+                       (L ~ U[16384,131072]): index_decode + topk_select +
+                       sparse_attn_decode, tokens/s
+  tiny_f32_512         index_prefill + sparse_attn_prefill on B=1, n=512,
+                       H^I=4, d^I=32, k=64, fp32 (report only: launch-bound)
 
 Timing: W untimed warm-up calls, then exactly K calls between two device
 synchronisations (wall clock; `value` and ms_per_step use it), with HIP
@@ -195,6 +200,24 @@ def bench_attn_dense(n, seed, steps, warmup):
                 peak_tflops=PEAK_BF16_TFLOPS, frac=ach / PEAK_BF16_TFLOPS, **tm.as_dict())
 
 
+def bench_tiny(steps, warmup):
+    """The tiny fp32 configuration (dyadic indexer inputs, exact scores):
+    index_prefill and sparse_attn_prefill timed separately; report only."""
+    B, n, HI, DI, k, H, Dqk, Dv = 1, 512, 4, 32, 64, 4, 80, 64
+    inp = synth.indexer_prefill(B, n, HI, DI, synth.DT_F32, 1, dist="dyadic", device=DEV)
+    ws = torch.empty(tl.index_prefill_workspace_bytes(inp.q, inp.k, inp.w, k), dtype=torch.uint8, device=DEV)
+    S = torch.empty((B, n, k), dtype=torch.int32, device=DEV)
+    ti = time_calls(lambda: tl.index_prefill(inp.q, inp.k, inp.w, k, S=S, workspace=ws), steps, warmup)
+    q, kv = synth.attn_prefill(B, n, H, Dqk, synth.DT_F32, 1, device=DEV)
+    out = torch.empty((B, n, H, Dv), dtype=torch.float32, device=DEV)
+    ta = time_calls(lambda: tl.sparse_attn_prefill(q, kv, S, 1.0 / math.sqrt(Dqk), Dv, out=out), steps, warmup)
+    pairs = causal_pairs(B, n)
+    log(f"tiny f32 n={n}: index_prefill {ti.ev_med * 1e3:.1f} us, sparse_attn_prefill {ta.ev_med * 1e3:.1f} us")
+    return dict(workload=f"tiny prefill: B=1, n={n}, H^I={HI}, d^I={DI}, k={k}, f32 dyadic; attention H={H}, "
+                         f"Dqk={Dqk}, Dv={Dv}, f32 (report only: launch-bound)",
+                pairs_per_s=pairs / (ti.wall * 1e-3), index_prefill=ti.as_dict(), sparse_attn_prefill=ta.as_dict())
+
+
 def decode_bytes(lengths, HI, DI, H, Dqk, Dv, k):
     """Algorithmic HBM bytes of one decode step (score round trip excluded)."""
     L = np.asarray(lengths, dtype=np.float64)
@@ -342,22 +365,15 @@ def cpu_baseline(inp, k, n, target_s=15.0):
                        f"({pairs} causal pairs, {dt:.1f} s, double precision, OpenMP over rows)")
 
 
-# HBM traffic of the headline kernel per launch, from two rocprofv3 --pmc runs of
-# `bench.py --no-cpu --only decode --steps 3 --warmup 1` (FETCH_SIZE, then WRITE_SIZE,
-# KiB per dispatch, averaged over the dispatches of the kernel), each scaled by
-# the same counter's reading for the 1 GiB calibration copy (the reading that
-# counts the copy's writes exactly; see profiles/prefill_score_kernel_bf16_n8192.md).
-# The figures hold only for the kernel sources they were taken on: when the
-# hash of those sources differs, the traffic is reported as null.
+# HBM traffic of a kernel per launch on one workload, from two rocprofv3 --pmc
+# runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, averaged over the
+# kernel's dispatches), each scaled by the same counter's reading for the
+# 1 GiB calibration copy of the same run (the reading that counts the copy's
+# bytes exactly).  The figures hold only for the kernel sources they were
+# taken on: when the hash of those sources differs, traffic is reported as
+# null.  Commands and readings: profiles/prefill_score_kernel_fp8_n131072.md.
 TRAFFIC_SOURCES = ("indexer.hip", "tlsl_device.h", "tlsl_internal.h", "topk_common.h")
-TRAFFIC = {
-    # profiles/prefill_score_kernel_bf16_n8192.md
-    "prefill_score_kernel": {
-        "sources_sha256": "848709082d78f13485d39216b597162e4cf04d8960f2fd8cd033ca121fb9af4d",
-        "fetch_kib": 85372.9062, "write_kib": 168480.1562,
-        "copy_fetch_kib": 524302.1429, "copy_write_kib": 1048576.0, "copy_bytes": 1 << 30,
-    },
-}
+TRAFFIC = {}
 
 
 def sources_sha256(names):
@@ -369,12 +385,16 @@ def sources_sha256(names):
     return h.hexdigest()
 
 
-def recorded_traffic(kernel):
-    rec = TRAFFIC.get(kernel)
+def recorded_traffic(kernel, workload):
+    rec = TRAFFIC.get((kernel, workload))
     if not rec or rec["sources_sha256"] != sources_sha256(TRAFFIC_SOURCES):
         return None
     copy = float(rec["copy_bytes"])
     return (rec["fetch_kib"] * copy / rec["copy_fetch_kib"] + rec["write_kib"] * copy / rec["copy_write_kib"])
+
+
+EXTRAS = ("attn_prefill_131072", "prefill_bf16_8192", "prefill_fp8_32768", "attn_prefill_32768",
+          "attn_dense_2048", "decode", "tiny_f32_512")
 
 
 def main():
@@ -382,11 +402,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--seed", type=int, default=2)
-    ap.add_argument("--long", action="store_true", help="also time the n=131072 prefill")
     ap.add_argument("--quick", action="store_true", help="headline workload (and calibration) only")
-    ap.add_argument("--only", default="", help="comma list of extra workloads to run: "
-                    "prefill_fp8,attn_prefill,attn_dense,decode,prefill_long (default: all but prefill_long)")
+    ap.add_argument("--only", default="", help="comma list of extra workloads to run (default: all of "
+                    + ",".join(EXTRAS) + ")")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-calib", action="store_true", help="skip the copy and matrix-core calibration")
     args = ap.parse_args()
@@ -396,46 +414,57 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     tl.load()
+    want = set() if args.quick else (set(args.only.split(",")) if args.only else set(EXTRAS))
+    unknown = want - set(EXTRAS)
+    if unknown:
+        print(f"unknown workloads {sorted(unknown)}; choose from {EXTRAS}", file=sys.stderr)
+        sys.exit(2)
 
-    head, inp, S = bench_prefill(8192, synth.DT_BF16, args.seed, args.steps, args.warmup)
-    # the headline inputs stay on the host for the CPU baseline and are freed
-    # on the device before the other workloads
-    inp = synth.IndexerPrefill(inp.dt, inp.q.cpu(), None if inp.q_scale is None else inp.q_scale.cpu(), inp.k.cpu(),
-                               None if inp.k_scale is None else inp.k_scale.cpu(), inp.w.cpu(), inp.probes)
-    del S
+    N_HEAD, K_HEAD, SEED_HEAD = 131072, 2048, 5
+    head, inp, S = bench_prefill(N_HEAD, synth.DT_FP8, SEED_HEAD, args.steps, args.warmup, plant_max_dist=100000)
+    # the headline inputs go to the host for the CPU baseline and are freed on
+    # the device before the other workloads
+    inp = synth.IndexerPrefill(inp.dt, inp.q.cpu(), inp.q_scale.cpu(), inp.k.cpu(), inp.k_scale.cpu(), inp.w.cpu(),
+                               inp.probes)
     torch.cuda.empty_cache()
     extra = {}
-    want = set(args.only.split(",")) if args.only else {"prefill_fp8", "attn_prefill", "attn_dense", "decode"}
-    if args.long:
-        want.add("prefill_long")
-    if not args.quick:
-        if want & {"prefill_fp8", "attn_prefill"}:
-            fp8, _, S3 = bench_prefill(32768, synth.DT_FP8, args.seed + 1, max(5, args.steps // 2), 2)
-            extra["prefill_fp8"] = fp8
-            if "attn_prefill" in want:
-                extra["attn_prefill"] = bench_attn_prefill(S3, 32768, args.seed + 1, max(3, args.steps // 4), 1)
-            del S3
-            torch.cuda.empty_cache()
-        if "attn_dense" in want:
-            extra["attn_dense"] = bench_attn_dense(2048, args.seed + 2, max(5, args.steps // 2), 2)
-            torch.cuda.empty_cache()
-        if "decode" in want:
-            extra["decode"] = bench_decode(args.seed + 3, args.steps, args.warmup)
-            torch.cuda.empty_cache()
-        if "prefill_long" in want:
-            lg, _, _ = bench_prefill(131072, synth.DT_FP8, args.seed + 4, 3, 1, plant_max_dist=100000)
-            extra["prefill_long"] = lg
+    if "attn_prefill_131072" in want:
+        extra["attn_prefill_131072"] = bench_attn_prefill(S, N_HEAD, SEED_HEAD, max(3, args.steps // 4), 1)
+    del S
+    torch.cuda.empty_cache()
+    if "prefill_bf16_8192" in want:
+        extra["prefill_bf16_8192"], _, S2 = bench_prefill(8192, synth.DT_BF16, 2, args.steps, args.warmup)
+        del S2
+        torch.cuda.empty_cache()
+    if want & {"prefill_fp8_32768", "attn_prefill_32768"}:
+        fp8, _, S3 = bench_prefill(32768, synth.DT_FP8, 3, max(5, args.steps // 2), 2)
+        if "prefill_fp8_32768" in want:
+            extra["prefill_fp8_32768"] = fp8
+        if "attn_prefill_32768" in want:
+            extra["attn_prefill_32768"] = bench_attn_prefill(S3, 32768, 3, max(3, args.steps // 4), 1)
+        del S3
+        torch.cuda.empty_cache()
+    if "attn_dense_2048" in want:
+        extra["attn_dense_2048"] = bench_attn_dense(2048, 6, max(5, args.steps // 2), 2)
+        torch.cuda.empty_cache()
+    if "decode" in want:
+        extra["decode"] = bench_decode(4, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+    if "tiny_f32_512" in want:
+        extra["tiny_f32_512"] = bench_tiny(args.steps, args.warmup)
+        torch.cuda.empty_cache()
     calib = None if args.no_calib else calibrate(args.steps)
-    cpu = None if args.no_cpu else cpu_baseline(inp, 2048, 8192)
+    cpu = None if args.no_cpu else cpu_baseline(inp, K_HEAD, N_HEAD)
 
-    roofline = {"bound": "mfma", "achieved": head["kernel_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": head["frac"], "traffic": recorded_traffic("prefill_score_kernel"),
+    roofline = {"bound": "mfma", "achieved": head["kernel_tflops"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": head["frac"],
+                "traffic": recorded_traffic("prefill_score_kernel", "fp8_n131072"),
                 "kernel": "prefill_score_kernel", "kernel_ms": head["kernel_ms_avg"],
                 "launches": head["kernel_launches"], "flops_per_launch": head["flops_per_call"],
                 "algorithmic_bytes_per_launch": head["algorithmic_bytes_per_call"]}
     if calib:
-        roofline["measured_peak"] = calib["mfma_bf16_tflops"]
-        roofline["frac_of_measured_peak"] = head["kernel_tflops"] / calib["mfma_bf16_tflops"]
+        roofline["measured_peak"] = calib["mfma_fp8_tflops"]
+        roofline["frac_of_measured_peak"] = head["kernel_tflops"] / calib["mfma_fp8_tflops"]
     line = {
         "metric": "indexer+top-k query-key pairs/s (prefill)",
         "value": head["pairs_per_s"],
@@ -447,10 +476,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3",
         "data": "synthetic",
-        "config": {"workload": head["workload"], "B": 1, "n": 8192, "H_I": 64, "d_I": 128, "k": 2048,
-                   "seed": args.seed},
+        "config": {"workload": head["workload"], "B": 1, "n": N_HEAD, "H_I": 64, "d_I": 128, "k": K_HEAD,
+                   "indexer_dtype": "fp8_e4m3 with per-token fp32 scales", "seed": SEED_HEAD},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "headline": head,

@@ -39,7 +39,12 @@
  *  - Results are bitwise reproducible for identical inputs and shapes.
  *  - fp8 means OCP e4m3 (e4m3fn: bias 7, max 448, no infinities), the format
  *    gfx950's matrix cores take, with one fp32 scale per token: a value is
- *    scale * code.
+ *    scale * code.  Scales must be finite and > 0: the kernels take them out
+ *    of the ReLU and the head sum (w is multiplied by the query's scale, the
+ *    head-summed score by the key's), which equals ReLU(scale_q * scale_k *
+ *    q.k) only for positive scales.  The scales live in device memory and are
+ *    not checked; a zero, negative or non-finite scale gives unspecified
+ *    scores.
  */
 #ifndef TLSL_H
 #define TLSL_H
@@ -106,9 +111,12 @@ int index_prefill(const void* qI, const float* q_scale, const void* kI, const fl
  *   k_scale    [sumL] fp32               (fp8 only; NULL otherwise)
  *   wI         [B,HI] fp32
  *   cu_seqlens [B+1] int64 (device), non-decreasing, cu_seqlens[0] = 0
- *   max_len    >= every L_b (host value; sizes the launch)
+ *   max_len    should be >= every L_b (host value; it sizes the launch and
+ *              any staging; a longer sequence is still scored in full, only
+ *              more slowly)
  *   scores     [sumL] fp32 out, packed like the cache
- * Supported shapes as index_prefill.  Sequences with L_b = 0 are skipped.
+ * Supported shapes as index_prefill; L_b < 2^31 - 2^12.  Sequences with
+ * L_b = 0 are skipped.
  */
 int index_decode(const void* qI, const float* q_scale, const void* kI_cache,
                  const float* k_scale, const float* wI, const int64_t* cu_seqlens, int B,
@@ -123,10 +131,11 @@ int index_decode(const void* qI, const float* q_scale, const void* kI_cache,
  *
  *   scores    fp32 (device)
  *   row_start [R] int64 (device), row_len [R] int32 (device, >= 0)
- *   max_len   >= every row_len (host value)
+ *   max_len   should be >= every row_len (host value; it sizes the launch;
+ *             a longer row is still selected exactly, only more slowly)
  *   S         [R,k] int32 out, S_score [R,k] fp32 out (optional)
  *   workspace about R*(2k+264)*8 bytes (query protocol above)
- * Supported: 1 <= k <= 4096, 0 <= row_len < 2^31.
+ * Supported: 1 <= k <= 4096, 0 <= row_len < 2^31 - 2^12.
  */
 int topk_select(const float* scores, const int64_t* row_start, const int32_t* row_len, int R,
                 int k, int max_len, int32_t* S, float* S_score, void* workspace,

@@ -55,6 +55,7 @@ def _load():
                                                      ctypes.c_double, P, I, P, P]
         lib.ora_sparse_attn_decode.argtypes = [I, P, P, P, P, I, I, I, I, I, ctypes.c_double,
                                                P, I, P, P]
+        lib.ora_sparse_attn_rows.argtypes = [I, P, P, P, P, I, I, I, I, I, ctypes.c_double, P, P]
         lib.ora_num_threads.restype = I
         _lib = lib
     return _lib
@@ -190,4 +191,24 @@ def sparse_attn_decode(dt, q, kv, cu_seqlens, S, scale, Dv, seqs=None):
     _check(lib.ora_sparse_attn_decode(dt, _ptr(q), _ptr(kv), _ptr(cu), _ptr(S), B, H, Dqk, Dv,
                                       k, float(scale), _ptr(seqs), len(seqs), _ptr(out),
                                       _ptr(lse)), "sparse_attn_decode")
+    return out, lse
+
+
+def sparse_attn_rows(dt, q_rows, kv, S_rows, limits, scale, Dv):
+    """eq.(3) for query rows given one by one: q_rows [R,H,Dqk], their slots
+    S_rows [R,k] into the entries kv [m,Dqk], valid slots 0 <= s <= limits[r].
+    Returns (out[R,H,Dv] f64, lse[R,H])."""
+    lib = _load()
+    q_rows = _c(q_rows)
+    kv = _c(kv)
+    S_rows = _c(S_rows, np.int32)
+    limits = _c(limits, np.int64)
+    R, H, Dqk = q_rows.shape
+    k = S_rows.shape[-1]
+    if S_rows.shape[0] != R or len(limits) != R or kv.shape[-1] != Dqk:
+        raise ValueError("oracle sparse_attn_rows: inconsistent shapes")
+    out = np.empty((R, H, Dv), np.float64)
+    lse = np.empty((R, H), np.float64)
+    _check(lib.ora_sparse_attn_rows(dt, _ptr(q_rows), _ptr(kv), _ptr(S_rows), _ptr(limits), R, H, Dqk,
+                                    Dv, k, float(scale), _ptr(out), _ptr(lse)), "sparse_attn_rows")
     return out, lse

@@ -41,6 +41,8 @@ class SelectionReport:
     structure_errors: list = field(default_factory=list)
     margin_errors: list = field(default_factory=list)
     exact_errors: list = field(default_factory=list)
+    mismatched_rows: int = 0
+    worst_margin_ratio: float = 0.0   # max over mismatches of |I(t,s) - c_t| / tolerance
 
     @property
     def match(self) -> float:
@@ -55,6 +57,7 @@ class SelectionReport:
 
     def summary(self) -> str:
         return (f"rows={self.rows} slots={self.slots} match={self.match:.6f} "
+                f"mismatched_rows={self.mismatched_rows} worst_margin_ratio={self.worst_margin_ratio:.3g} "
                 f"structure={self.structure_errors[:3]} margin={self.margin_errors[:3]} "
                 f"exact={self.exact_errors[:3]}")
 
@@ -100,12 +103,14 @@ def check_selection(S_gpu, S_ora, ts, k, score_rows=None, exact=False) -> Select
         gs, os_ = set(g[:K].tolist()), set(o[:K].tolist())
         rep.matched += len(gs & os_)
         diff = gs ^ os_
+        rep.mismatched_rows += bool(diff)
         if diff and score_rows is not None:
             sr = np.asarray(score_rows[i], dtype=np.float64)
             c = kth_score(sr, t, K)
             floor = 1e-6 * float(np.abs(sr[: t + 1]).max())
             tol = MARGIN_RTOL * max(abs(c), floor)
             worst = max(abs(sr[s] - c) for s in diff)
+            rep.worst_margin_ratio = max(rep.worst_margin_ratio, worst / tol if tol > 0 else float("inf"))
             if worst > tol:
                 rep.margin_errors.append((t, len(diff), worst, tol))
         elif diff and not exact:

@@ -384,6 +384,31 @@ int ora_sparse_attn_decode(int dt, const void *q, const void *kv, const int64_t 
     return 0;
 }
 
+/* The same attention for rows given one by one: query r (q_rows[r], H x Dqk)
+ * attends over its slots S_rows[r] (k of them) into entries kv[0..], valid
+ * slots 0 <= s <= limits[r].  For a prefill row t of batch row b this is
+ * kv = that batch row's entries and limit t: the rows a test samples from a
+ * large batch are evaluated without the whole query tensor. */
+int ora_sparse_attn_rows(int dt, const void *q_rows, const void *kv, const int32_t *S_rows,
+                         const int64_t *limits, int nrows, int H, int Dqk, int Dv, int k,
+                         double scale, double *out, double *lse)
+{
+    if (!q_rows || !kv || !S_rows || !limits || !out || nrows < 0 || H <= 0 || Dv > Dqk || k <= 0)
+        return -1;
+    if (dt == ORA_FP8)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; ++r) {
+        double *qq = malloc(sizeof(double) * (size_t)H * Dqk);
+        for (int64_t j = 0; j < (int64_t)H * Dqk; ++j)
+            qq[j] = load_elem(dt, q_rows, (int64_t)r * H * Dqk + j);
+        attend_row(dt, qq, kv, 0, S_rows + (int64_t)r * k, k, limits[r], H, Dqk, Dv, scale,
+                   out + (int64_t)r * H * Dv, lse ? lse + (int64_t)r * H : NULL);
+        free(qq);
+    }
+    return 0;
+}
+
 int ora_num_threads(void)
 {
     int n = 1;

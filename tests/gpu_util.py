@@ -30,3 +30,14 @@ def sample_rows(n, k, count, seed=0, extra=()):
     rng = np.random.default_rng(seed)
     rest = rng.choice(n, size=min(n, count), replace=False)
     return np.array(sorted({int(x) for x in base if 0 <= x < n} | {int(x) for x in rest}), dtype=np.int64)
+
+
+def stratified_rows(n, k, probes=(), uniform=0, seed=0):
+    """The stratified query-row sample of the full-size checks: the edges of
+    the selection rule t in {0, k-2, k-1, k, n-1} (where min(k, t+1) switches
+    from "every position" to a real selection), every probe row (the queries
+    with planted keys), and ``uniform`` more rows drawn uniformly."""
+    base = {0, k - 2, k - 1, k, n - 1} | {int(t) for t in probes}
+    rng = np.random.default_rng(seed)
+    extra = rng.choice(n, size=min(n, uniform), replace=False) if uniform else []
+    return np.array(sorted(t for t in base | {int(x) for x in extra} if 0 <= t < n), dtype=np.int64)

@@ -1,0 +1,104 @@
+// abi_driver.cpp -- drives every entry point of include/tlsl.h through its
+// validation and workspace-query paths and one accepted call each, against the
+// launcher stand-ins of abi_stubs.cpp.  Built and run under ASan + UBSan by
+// tests/test_sanitizers.py; prints "abi driver ok" and exits 0 when every
+// return code is the documented one.  TEST INFRASTRUCTURE ONLY.
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/tlsl.h"
+
+extern int g_launches;
+static int g_fail = 0;
+
+#define EXPECT(call, code)                                                                       \
+    do {                                                                                         \
+        const int rc_ = (call);                                                                  \
+        if (rc_ != (code)) {                                                                     \
+            fprintf(stderr, "line %d: %s returned %d, expected %d (%s)\n", __LINE__, #call, rc_, \
+                    (int)(code), tlsl_last_error());                                             \
+            ++g_fail;                                                                            \
+        }                                                                                        \
+    } while (0)
+
+int main() {
+    // dummy device pointers: 16-byte aligned, never dereferenced by the host layer
+    void* P = reinterpret_cast<void*>(uintptr_t(0x10000));
+    float* F = static_cast<float*>(P);
+    int32_t* I32 = static_cast<int32_t*>(P);
+    int64_t* I64 = static_cast<int64_t*>(P);
+    void* odd = reinterpret_cast<void*>(uintptr_t(0x10004));
+    size_t ws = 0, need = 0;
+
+    // ---- index_prefill
+    EXPECT(index_prefill(P, F, P, F, F, 1, 100, 64, 128, 16, TLSL_FP8_E4M3, I32, F, nullptr, &need, nullptr), TLSL_OK);
+    if (need == 0) { fprintf(stderr, "index_prefill: zero workspace\n"); ++g_fail; }
+    ws = need - 1;
+    EXPECT(index_prefill(P, F, P, F, F, 1, 100, 64, 128, 16, TLSL_FP8_E4M3, I32, F, P, &ws, nullptr), TLSL_ERR_WORKSPACE);
+    ws = need;
+    EXPECT(index_prefill(P, F, P, F, F, 1, 100, 64, 128, 16, TLSL_FP8_E4M3, I32, F, P, &ws, nullptr), TLSL_OK);
+    EXPECT(index_prefill(P, F, P, F, F, 1, 100, 64, 128, 16, TLSL_FP8_E4M3, I32, F, P, nullptr, nullptr), TLSL_ERR_NULL);
+    EXPECT(index_prefill(nullptr, F, P, F, F, 1, 100, 64, 128, 16, TLSL_FP8_E4M3, I32, F, P, &ws, nullptr), TLSL_ERR_NULL);
+    EXPECT(index_prefill(P, nullptr, P, F, F, 1, 100, 64, 128, 16, TLSL_FP8_E4M3, I32, F, P, &ws, nullptr), TLSL_ERR_NULL);
+    EXPECT(index_prefill(P, F, P, F, F, 1, 100, 64, 128, 16, TLSL_BF16, I32, F, P, &ws, nullptr), TLSL_ERR_SHAPE);
+    EXPECT(index_prefill(P, nullptr, P, nullptr, F, 0, 100, 64, 128, 16, TLSL_BF16, I32, F, P, &ws, nullptr), TLSL_ERR_SHAPE);
+    EXPECT(index_prefill(P, nullptr, P, nullptr, F, 1, 100, 64, 128, 0, TLSL_BF16, I32, F, P, &ws, nullptr), TLSL_ERR_SHAPE);
+    EXPECT(index_prefill(P, nullptr, P, nullptr, F, 1, 100, 64, 128, 4097, TLSL_BF16, I32, F, P, &ws, nullptr), TLSL_ERR_UNSUPPORTED);
+    EXPECT(index_prefill(P, nullptr, P, nullptr, F, 1, 100, 65, 128, 16, TLSL_BF16, I32, F, P, &ws, nullptr), TLSL_ERR_UNSUPPORTED);
+    EXPECT(index_prefill(P, nullptr, P, nullptr, F, 1, 100, 64, 96, 16, TLSL_BF16, I32, F, P, &ws, nullptr), TLSL_ERR_UNSUPPORTED);
+    EXPECT(index_prefill(P, nullptr, P, nullptr, F, 1, 100, 64, 128, 16, (tlsl_dtype)7, I32, F, P, &ws, nullptr), TLSL_ERR_UNSUPPORTED);
+    EXPECT(index_prefill(odd, nullptr, P, nullptr, F, 1, 100, 64, 128, 16, TLSL_BF16, I32, F, P, &ws, nullptr), TLSL_ERR_ALIGN);
+    EXPECT(index_prefill(P, nullptr, P, nullptr, F, 1 << 16, 1 << 15, 64, 128, 16, TLSL_BF16, I32, F, P, &ws, nullptr), TLSL_ERR_SHAPE);
+
+    // ---- index_decode
+    EXPECT(index_decode(P, F, P, F, F, I64, 4, 64, 128, 1000, TLSL_FP8_E4M3, F, nullptr, &ws, nullptr), TLSL_OK);
+    if (ws != 0) { fprintf(stderr, "index_decode: nonzero workspace\n"); ++g_fail; }
+    EXPECT(index_decode(P, F, P, F, F, nullptr, 4, 64, 128, 1000, TLSL_FP8_E4M3, F, nullptr, &ws, nullptr), TLSL_ERR_NULL);
+    EXPECT(index_decode(P, F, P, F, F, I64, 0, 64, 128, 1000, TLSL_FP8_E4M3, F, nullptr, &ws, nullptr), TLSL_ERR_SHAPE);
+    EXPECT(index_decode(P, F, P, F, F, I64, 4, 64, 128, 0, TLSL_FP8_E4M3, F, nullptr, &ws, nullptr), TLSL_ERR_SHAPE);
+    EXPECT(index_decode(P, F, P, F, F, I64, 4, 64, 128, 1000, TLSL_FP8_E4M3, static_cast<float*>(odd), nullptr, &ws, nullptr), TLSL_ERR_ALIGN);
+
+    // ---- topk_select
+    EXPECT(topk_select(F, I64, I32, 64, 2048, 131072, I32, F, nullptr, &need, nullptr), TLSL_OK);
+    ws = need;
+    EXPECT(topk_select(F, I64, I32, 64, 2048, 131072, I32, F, P, &ws, nullptr), TLSL_OK);
+    ws = need / 2;
+    EXPECT(topk_select(F, I64, I32, 64, 2048, 131072, I32, F, P, &ws, nullptr), TLSL_ERR_WORKSPACE);
+    EXPECT(topk_select(F, I64, I32, 0, 2048, 131072, I32, F, nullptr, &need, nullptr), TLSL_ERR_SHAPE);
+    EXPECT(topk_select(F, I64, I32, 64, 5000, 131072, I32, F, nullptr, &need, nullptr), TLSL_ERR_UNSUPPORTED);
+    EXPECT(topk_select(F, I64, I32, 64, 2048, -1, I32, F, nullptr, &need, nullptr), TLSL_ERR_SHAPE);
+    EXPECT(topk_select(static_cast<float*>(reinterpret_cast<void*>(uintptr_t(0x10002))), I64, I32, 64, 2048, 10, I32,
+                       F, nullptr, &need, nullptr), TLSL_ERR_ALIGN);
+
+    // ---- attention
+    const float sc = 0.05f;
+    EXPECT(sparse_attn_prefill(P, P, I32, 1, 100, 128, 576, 512, 2048, sc, TLSL_BF16, P, F, nullptr, &ws, nullptr), TLSL_OK);
+    EXPECT(sparse_attn_prefill(P, P, I32, 1, 100, 129, 576, 512, 2048, sc, TLSL_BF16, P, F, nullptr, &ws, nullptr), TLSL_ERR_UNSUPPORTED);
+    EXPECT(sparse_attn_prefill(P, P, I32, 1, 100, 128, 576, 512, 2048, -1.f, TLSL_BF16, P, F, nullptr, &ws, nullptr), TLSL_ERR_SHAPE);
+    EXPECT(sparse_attn_prefill(P, P, I32, 1, 100, 128, 576, 512, 2048, INFINITY, TLSL_BF16, P, F, nullptr, &ws, nullptr), TLSL_ERR_SHAPE);
+    EXPECT(sparse_attn_prefill(P, P, I32, 1, 100, 128, 576, 512, 2048, NAN, TLSL_BF16, P, F, nullptr, &ws, nullptr), TLSL_ERR_SHAPE);
+    EXPECT(sparse_attn_prefill(P, P, I32, 1, 100, 4, 80, 64, 64, sc, TLSL_FP8_E4M3, P, F, nullptr, &ws, nullptr), TLSL_ERR_UNSUPPORTED);
+    EXPECT(dense_attn_prefill(P, P, 1, 4096, 128, 576, 512, sc, TLSL_BF16, P, F, nullptr, &ws, nullptr), TLSL_OK);
+    EXPECT(dense_attn_prefill(P, P, 1, 4097, 128, 576, 512, sc, TLSL_BF16, P, F, nullptr, &ws, nullptr), TLSL_ERR_UNSUPPORTED);
+    EXPECT(sparse_attn_decode(P, P, I64, I32, 64, 128, 576, 512, 2048, sc, TLSL_BF16, P, F, nullptr, &need, nullptr), TLSL_OK);
+    ws = need;
+    EXPECT(sparse_attn_decode(P, P, I64, I32, 64, 128, 576, 512, 2048, sc, TLSL_BF16, P, F, P, &ws, nullptr), TLSL_ERR_HIP);
+    if (strstr(tlsl_last_error(), "stubbed HIP error") == nullptr) {
+        fprintf(stderr, "launch error message not reported: %s\n", tlsl_last_error());
+        ++g_fail;
+    }
+    EXPECT(sparse_attn_decode(P, P, I64, I32, 64, 128, 576, 512, 2048, sc, TLSL_BF16, P, F, nullptr, nullptr, nullptr), TLSL_ERR_NULL);
+    if (strlen(tlsl_version()) == 0) ++g_fail;
+
+    // accepted calls: index_prefill, index_decode, topk_select, sparse_attn_prefill,
+    // dense_attn_prefill, sparse_attn_decode (the last one's stand-in fails on purpose)
+    if (g_launches != 6) {
+        fprintf(stderr, "expected 6 launches, saw %d\n", g_launches);
+        ++g_fail;
+    }
+    if (g_fail) return 1;
+    printf("abi driver ok\n");
+    return 0;
+}

@@ -360,3 +360,120 @@ def test_sparse_attn_decode(dt, H, Dqk, Dv):
     err = np.abs(out.float().cpu().numpy() - ref).max()
     assert err <= tol, err
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
+
+
+# ---------------------------------------------------------------------------
+# the DSA page's worked example (section 1.1, eq.(4)-(6)) on the GPU
+# ---------------------------------------------------------------------------
+def _golden():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("dt,DI", [(F32, 32), (BF16, 32), (FP8, 128)])
+def test_worked_example_on_gpu(dt, DI):
+    """The 3-token example, its two dims zero-padded to a built d^I: the padded
+    dims add exact zeros, so the scores are exactly 1.5, 1.5, 1.0 and the
+    selection at k=2 is {0, 1} (1-based {1, 2}); at k=1 the 1.5/1.5 tie goes
+    to the lower position.  Prefill (query at t=2) and decode (one sequence of
+    length 3, then topk_select) must both give it."""
+    ex = _golden()["indexer"]
+    HI = ex["H_I"]
+    q = torch.zeros(1, 3, HI, DI)
+    q[0, 2, :, :2] = torch.tensor(ex["q"], dtype=torch.float32)
+    kk = torch.zeros(1, 3, DI)
+    kk[0, :, :2] = torch.tensor(ex["keys"], dtype=torch.float32)
+    w = torch.zeros(1, 3, HI)
+    w[0, 2] = torch.tensor(ex["w"], dtype=torch.float32)
+    if dt == FP8:
+        # unit scales keep the small integers exact in e4m3
+        qs = q.to(torch.float8_e4m3fn).view(torch.uint8)
+        ks = kk.to(torch.float8_e4m3fn).view(torch.uint8)
+        q_scale, k_scale = torch.ones(1, 3), torch.ones(1, 3)
+    else:
+        qs = q.to(torch.bfloat16) if dt == BF16 else q
+        ks = kk.to(torch.bfloat16) if dt == BF16 else kk
+        q_scale = k_scale = None
+    announce(f"worked example dt={dt} DI={DI}")
+    for k, want in ((ex["k"], [p - 1 for p in ex["selected_1based"]]), (1, [0]), (4, [0, 1, 2, -1])):
+        S, Ss = tl.index_prefill(to_dev(qs), to_dev(ks), to_dev(w), k, q_scale=to_dev(q_scale),
+                                 k_scale=to_dev(k_scale), want_scores=True)
+        torch.cuda.synchronize()
+        assert S[0, 2].tolist() == want, (k, S[0, 2].tolist())
+        exp_sc = [ex["scores"][p] if p >= 0 else -math.inf for p in want]
+        assert Ss[0, 2].tolist() == exp_sc
+    # decode: the same query against the 3-key cache
+    cu = torch.tensor([0, 3], dtype=torch.int64)
+    sc = tl.index_decode(to_dev(qs[0, 2:3]), to_dev(ks[0]), to_dev(w[0, 2:3]), to_dev(cu), 3,
+                         q_scale=to_dev(None if q_scale is None else q_scale[0, 2:3]),
+                         k_scale=to_dev(None if k_scale is None else k_scale[0]))
+    Sd, _ = tl.topk_select(sc, to_dev(cu[:1]), to_dev(torch.tensor([3], dtype=torch.int32)), ex["k"], 3)
+    torch.cuda.synchronize()
+    assert sc.cpu().tolist() == ex["scores"]
+    assert Sd[0].tolist() == [p - 1 for p in ex["selected_1based"]]
+
+
+def test_worked_example_attention_on_gpu():
+    """eq.(5)-(6) of the example: logits 0.2 and 1.2 over values (2,0) and
+    (0,3) give weights (0.269, 0.731) and output (0.538, 2.193).  Encoded in
+    the fp32 build (Dqk = 80 = 64 value dims + 16 position dims): the values in
+    dims 0-1, the logit in position dim 64, q = e_64, scale 1."""
+    ex = _golden()["attention"]
+    kv = torch.zeros(1, 3, 80)
+    for s, (v, z) in enumerate(zip(ex["values"], ex["logits"])):
+        kv[0, s, :2] = torch.tensor(v, dtype=torch.float32)
+        kv[0, s, 64] = z
+    q = torch.zeros(1, 3, 1, 80)
+    q[0, 2, 0, 64] = 1.0
+    S = torch.tensor([[[0, -1], [0, 1], [0, 1]]], dtype=torch.int32)
+    announce("worked example attention")
+    out, lse = tl.sparse_attn_prefill(to_dev(q), to_dev(kv), to_dev(S), 1.0, 64, want_lse=True)
+    torch.cuda.synchronize()
+    o = out[0, 2, 0].cpu().numpy()
+    d = ex["printed_decimals"]
+    assert [round(float(x), d) for x in o[:2]] == ex["output"]
+    assert (o[2:] == 0).all()
+    w = np.exp(np.array(ex["logits"]) - float(lse[0, 2, 0]))
+    assert [round(float(x), d) for x in w] == ex["weights"]
+
+
+# ---------------------------------------------------------------------------
+# index_decode batch sizes: a multiple of the scan's 256-thread prefix loop,
+# one past it, and the path for more than 4096 sequences
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B", [256, 257, 4100])
+def test_index_decode_batch_sizes(B):
+    rng = np.random.default_rng(B)
+    lengths = rng.integers(1, 300, size=B)
+    lengths[B // 3] = 0          # an empty sequence
+    lengths[-1] = 513            # the last sequence is the longest
+    inp = synth.indexer_decode(lengths, 64, 128, FP8, seed=B, planted=False)
+    announce(f"index_decode B={B} sumL={int(lengths.sum())}")
+    sc = tl.index_decode(to_dev(inp.q), to_dev(inp.k), to_dev(inp.w), to_dev(inp.cu_seqlens), int(lengths.max()),
+                         q_scale=to_dev(inp.q_scale), k_scale=to_dev(inp.k_scale))
+    torch.cuda.synchronize()
+    ref, mag = oracle.index_decode(FP8, host(inp.q), host(inp.q_scale), host(inp.k), host(inp.k_scale),
+                                   host(inp.w), host(inp.cu_seqlens))
+    got = sc.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert parity.check_score_vector(got, ref, mag, lowp=True) <= 1.0
+
+
+def test_max_len_below_the_lengths_is_still_exact():
+    """max_len only sizes the launch: a caller that passes a smaller value gets
+    every key scored and every row selected in full."""
+    lengths = np.array([9000, 30000, 5000, 17000])
+    inp = synth.indexer_decode(lengths, 64, 128, BF16, seed=21, planted=True)
+    announce("index_decode / topk_select with max_len below the lengths")
+    cu = to_dev(inp.cu_seqlens)
+    sc = tl.index_decode(to_dev(inp.q), to_dev(inp.k), to_dev(inp.w), cu, 1000)
+    sc_ok = tl.index_decode(to_dev(inp.q), to_dev(inp.k), to_dev(inp.w), cu, int(lengths.max()))
+    rl = to_dev(torch.tensor(lengths, dtype=torch.int32))
+    S_small, Ss_small = tl.topk_select(sc_ok, cu[:-1].contiguous(), rl, 2048, 100, want_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sc, sc_ok)
+    S_o, Ss_o = oracle.topk_rows(sc_ok.cpu().numpy(), host(inp.cu_seqlens)[:-1], lengths, 2048)
+    np.testing.assert_array_equal(S_small.cpu().numpy(), S_o)
+    np.testing.assert_array_equal(Ss_small.cpu().numpy(), Ss_o)

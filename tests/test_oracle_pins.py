@@ -345,3 +345,29 @@ def test_oracle_refuses_rows_outside_the_batch():
     cu = np.array([0, 4], np.int64)
     with pytest.raises(ValueError):
         oracle.sparse_attn_decode(0, q[:, 0], kv[0], cu, S[:, 0], 0.1, 64, seqs=np.array([1]))
+
+
+def test_row_form_of_attention_equals_batch_form():
+    """oracle.sparse_attn_rows (rows given one by one, as the full-size checks
+    use it) is the batch form's arithmetic with other marshalling: identical
+    results, also for rows whose slots hold -1, out-of-range positions and
+    duplicates."""
+    rng = np.random.default_rng(0)
+    B, n, H, D, Dv, k = 2, 50, 3, 8, 6, 10
+    q = rng.standard_normal((B, n, H, D)).astype(np.float32)
+    kv = rng.standard_normal((B, n, D)).astype(np.float32)
+    S = np.full((B, n, k), -1, np.int32)
+    for b in range(B):
+        for t in range(n):
+            K = min(k, t + 1)
+            S[b, t, :K] = np.sort(rng.choice(t + 1, K, replace=False))
+    S[1, 30, 0] = 45       # beyond t: skipped
+    S[1, 30, 2] = S[1, 30, 3]  # duplicate: counted twice
+    rows = np.array([0, 5, 17, 49, n + 30, n + 49])
+    a, al = oracle.sparse_attn_prefill_rows(synth.DT_F32, q, kv, S, 0.3, rows, Dv)
+    bb, t = rows // n, rows % n
+    for b in range(B):
+        sel = bb == b
+        r, rl = oracle.sparse_attn_rows(synth.DT_F32, q[b, t[sel]], kv[b], S[b, t[sel]], t[sel], 0.3, Dv)
+        np.testing.assert_array_equal(r, a[sel])
+        np.testing.assert_array_equal(rl, al[sel])

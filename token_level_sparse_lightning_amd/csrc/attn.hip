@@ -610,31 +610,6 @@ __global__ __launch_bounds__(CB_NT) void attn_combine_kernel(const float* part_o
 }
 
 // ---------------------------------------------------------------------------
-bool attn_supported(const AttnShape& s) {
-    if (s.dt == kBF16) return s.Dqk == 576 && s.Dv == 512 && s.H >= 1 && s.H <= 128;
-    if (s.dt == kF32) return s.Dqk == 80 && s.Dv == 64 && s.H >= 1 && s.H <= 16;
-    return false;
-}
-
-// Slot splits per decode row: about one workgroup per CU over the batch's rows
-// and head groups, at least 128 slots per split.
-static int decode_splits(const AttnShape& s, int B, int k) {
-    const int hpw = s.dt == kBF16 ? 64 : 16;
-    const int hg = (s.H + hpw - 1) / hpw;
-    const int cus = device_cu_count();
-    int ns = (cus + B * hg - 1) / (B * hg);
-    const int maxs = (k + 127) / 128;
-    if (ns > maxs) ns = maxs;
-    return ns < 1 ? 1 : ns;
-}
-
-size_t attn_decode_ws_bytes(const AttnShape& s, int B, int k) {
-    const int ns = decode_splits(s, B, k);
-    if (ns == 1) return 256;  // never empty, so that a NULL workspace always means "size query"
-    const size_t parts = (size_t)B * ns * s.H;
-    return parts * s.Dv * sizeof(float) + ((parts * 2 * sizeof(float) + 255) & ~(size_t)255) + 256;
-}
-
 template <int DT, int HBW, int DSPLIT, int DQK, int DV, bool DEC>
 static void launch_attn_t(AttnArgs a, int rows, hipStream_t st) {
     constexpr int HPW = 16 * HBW;
@@ -675,7 +650,7 @@ hipError_t launch_sparse_attn_prefill(const AttnShape& s, const void* q, const v
 hipError_t launch_sparse_attn_decode(const AttnShape& s, const void* q, const void* kv, const int64_t* cu,
                                      const int32_t* S, int B, int k, float scale, void* out, float* lse, void* ws,
                                      hipStream_t st) {
-    const int ns = decode_splits(s, B, k);
+    const int ns = attn_decode_splits(s, B, k);
     AttnArgs a{};
     a.q = static_cast<const unsigned char*>(q);
     a.kv = static_cast<const unsigned char*>(kv);

@@ -729,39 +729,43 @@ __global__ __launch_bounds__(DEC_NT) void decode_score_kernel(const unsigned cha
                                                               float* scores) {
     using I = Idx<DT, HB, DI>;
     constexpr int NCH = I::NCH;
-    const int b = blockIdx.y;
+    const int b = blockIdx.x;
     const int64_t start = cu[b];
     const int L = (int)(cu[b + 1] - start);
-    const int base = blockIdx.x * DEC_CHUNK;
-    if (base >= L) return;
+    if ((int64_t)blockIdx.y * DEC_CHUNK >= L) return;
     const int wv_id = threadIdx.x >> 6, l = lane_id();
     uint4 qf[HB][NCH];
     float wv[HB][4];
     const float wmul = (DT == kFP8) ? q_scale[b] : 1.f;
     I::load_query(q + (size_t)b * HI * I::ROWB, w + (size_t)b * HI, wmul, HI, true, qf, wv);
     const unsigned char* kb_base = kc + (size_t)start * I::ROWB;
-    const int end = min(L, base + DEC_CHUNK);
     constexpr int STEP = 64 * (DEC_NT / 64);
-    // two subtiles in flight per wave: the next one loads while this one is scored
-    uint4 kf[2][4][NCH];
-    int j0 = base + 64 * wv_id;
-    if (j0 < end) I::load_keys_global(kb_base, j0, L - 1, kf[0]);
-    for (; j0 < end; j0 += 2 * STEP) {
-        const int j1 = j0 + STEP;
-        if (j1 < end) I::load_keys_global(kb_base, j1, L - 1, kf[1]);
-        {
-            float s = I::score(qf, wv, kf[0]);
-            const int key = j0 + l;
-            if (DT == kFP8) s *= k_scale[start + min(key, L - 1)];
-            if (key < L) scores[start + key] = s;
-        }
-        if (j1 >= end) break;
-        if (j1 + STEP < end) I::load_keys_global(kb_base, j1 + STEP, L - 1, kf[0]);
-        {
-            float s = I::score(qf, wv, kf[1]);
-            const int key = j1 + l;
-            if (DT == kFP8) s *= k_scale[start + min(key, L - 1)];
-            if (key < L) scores[start + key] = s;
+    // chunks blockIdx.y, + gridDim.y, ...: a sequence longer than the launch
+    // was sized for (max_len) is still scored in full
+    for (int64_t base64 = (int64_t)blockIdx.y * DEC_CHUNK; base64 < L; base64 += (int64_t)gridDim.y * DEC_CHUNK) {
+        const int base = (int)base64;
+        const int end = min(L, base + DEC_CHUNK);
+        // two subtiles in flight per wave: the next one loads while this one is scored
+        uint4 kf[2][4][NCH];
+        int j0 = base + 64 * wv_id;
+        if (j0 < end) I::load_keys_global(kb_base, j0, L - 1, kf[0]);
+        for (; j0 < end; j0 += 2 * STEP) {
+            const int j1 = j0 + STEP;
+            if (j1 < end) I::load_keys_global(kb_base, j1, L - 1, kf[1]);
+            {
+                float s = I::score(qf, wv, kf[0]);
+                const int key = j0 + l;
+                if (DT == kFP8) s *= k_scale[start + min(key, L - 1)];
+                if (key < L) scores[start + key] = s;
+            }
+            if (j1 >= end) break;
+            if (j1 + STEP < end) I::load_keys_global(kb_base, j1 + STEP, L - 1, kf[0]);
+            {
+                float s = I::score(qf, wv, kf[1]);
+                const int key = j1 + l;
+                if (DT == kFP8) s *= k_scale[start + min(key, L - 1)];
+                if (key < L) scores[start + key] = s;
+            }
         }
     }
 }
@@ -836,7 +840,12 @@ __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned cha
         carry += tot;
         __syncthreads();
     }
-    if (tid == 0) pre[B] = carry;
+    // (the loop above writes sstart[B] only when B is not a multiple of
+    // DEC2_NT; the end of the last sequence is set here for every B)
+    if (tid == 0) {
+        pre[B] = carry;
+        sstart[B] = cu[B];
+    }
     __syncthreads();
     const int total = carry;
     const int per = (total + gridDim.x - 1) / gridDim.x;
@@ -941,44 +950,12 @@ int device_cu_count() {
     return cached[dev];
 }
 
-bool indexer_supported(const IndexerShape& s) {
-    if (s.HI < 1 || s.HI > 64) return false;
-    if (s.dt == kFP8) return s.DI == 128;
-    if (s.dt == kBF16) return s.DI == 32 || s.DI == 64 || s.DI == 128;
-    if (s.dt == kF32) return s.DI == 32 || s.DI == 64;
-    return false;
-}
-
 static int head_blocks(int HI) { return HI <= 16 ? 1 : (HI <= 32 ? 2 : 4); }
 static int queries_per_wave(const IndexerShape& s) {
     const int eb = s.dt == kF32 ? 4 : (s.dt == kBF16 ? 2 : 1);
     const int nch = s.DI * eb / 64;
     return nch * head_blocks(s.HI) <= 8 ? 2 : 1;
 }
-static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-PrefillPlan plan_prefill(const IndexerShape& s, int B, int n, int k) {
-    PrefillPlan p{};
-    p.cap = (int)((2 * (size_t)k + 256 + 255) / 256 * 256);
-    p.stride = std::max(1, k / 64);  // ~64 sample keys expected inside the top-k
-    p.fb_blocks = 128;
-    const size_t rows = (size_t)B * n;
-    size_t off = 0;
-    p.off_buf = off;
-    off = align256(off + rows * p.cap * sizeof(uint2));
-    p.off_cnt = off;
-    off = align256(off + rows * sizeof(int));
-    p.off_fbcount = off;
-    off = align256(off + sizeof(int));
-    p.off_fblist = off;
-    off = align256(off + rows * sizeof(int));
-    p.off_fbscratch = off;
-    off = align256(off + (size_t)p.fb_blocks * n * sizeof(float));
-    p.ws_bytes = off;
-    (void)s;
-    return p;
-}
-
 template <int DT, int HB, int DI>
 static hipError_t launch_prefill_t(const PrefillArgs& pa, const FinalizeArgs& fa, const FallbackArgs& fb,
                                    int qw, int rows, int cap, int fb_blocks, hipStream_t st) {
@@ -1083,11 +1060,18 @@ static hipError_t launch_decode_t(const void* q, const float* q_scale, const voi
         // fits, else a share per wave (flushed when full)
         constexpr int NWV = DEC2_NT / 64;
         const int64_t nsub_max = (int64_t)B * ((max_len + 63) / 64);
-        int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_scan_kernel<DT, HB, DI>, DEC2_NT,
-                                                         DEC2_LDS_BUDGET) != hipSuccess ||
-            nb < 1)
-            nb = 1;
+        // resident workgroups per CU, queried once per device and instantiation
+        static int occ[64] = {0};
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+        int nb = occ[dev];
+        if (nb == 0) {
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_scan_kernel<DT, HB, DI>, DEC2_NT,
+                                                             DEC2_LDS_BUDGET) != hipSuccess ||
+                nb < 1)
+                nb = 1;
+            occ[dev] = nb;
+        }
         const int grid = (int)std::min<int64_t>((int64_t)device_cu_count() * std::min(nb, 2), std::max<int64_t>(1, nsub_max));
         const int64_t per_max = (nsub_max + grid - 1) / grid;  // >= every workgroup's share
         const int64_t pw_max = (per_max + NWV - 1) / NWV;
@@ -1103,7 +1087,8 @@ static hipError_t launch_decode_t(const void* q, const float* q_scale, const voi
                                              scap, (int)(wg_stage ? per_max : 0)));
         return hipGetLastError();
     }
-    dim3 grid((max_len + DEC_CHUNK - 1) / DEC_CHUNK, B);
+    // one workgroup column per sequence (x), chunks of DEC_CHUNK keys (y)
+    dim3 grid(B, std::min((max_len + DEC_CHUNK - 1) / DEC_CHUNK, 65535));
     TLSL_TIMED_LAUNCH("decode_score_kernel", st,
                       hipLaunchKernelGGL((decode_score_kernel<DT, HB, DI>), grid, dim3(DEC_NT), 0, st,
                                          static_cast<const unsigned char*>(q), q_scale,

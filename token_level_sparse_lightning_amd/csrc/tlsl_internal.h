@@ -2,7 +2,7 @@
 // the kernels.  Launchers assume validated arguments.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -53,6 +53,13 @@ hipError_t launch_index_decode(const IndexerShape& s, const void* q, const float
                                hipStream_t st);
 
 // ---- row top-k ---------------------------------------------------------------
+constexpr int kTopkCntStride = 32;  // ints between two rows' candidate counters
+struct TopkLayout {
+    int cap;                                // candidate buffer entries per row
+    size_t off_theta, off_cnt, off_buf;     // workspace offsets
+    size_t bytes;                           // workspace size
+};
+TopkLayout topk_layout(int R, int k);
 size_t topk_ws_bytes(int R, int k, int max_len);
 hipError_t launch_topk_select(const float* scores, const int64_t* row_start,
                               const int32_t* row_len, int R, int k, int max_len, int32_t* S,
@@ -64,6 +71,8 @@ struct AttnShape {
     int H, Dqk, Dv;
 };
 bool attn_supported(const AttnShape& s);
+// slot splits per decode row (about one workgroup per compute unit)
+int attn_decode_splits(const AttnShape& s, int B, int k);
 size_t attn_decode_ws_bytes(const AttnShape& s, int B, int k);
 hipError_t launch_sparse_attn_prefill(const AttnShape& s, const void* q, const void* kv,
                                       const int32_t* S, int B, int n, int k, float scale,

@@ -16,6 +16,8 @@
 // The result never depends on the threshold, only the work does.
 #include <math.h>
 
+#include <algorithm>
+
 #include "tlsl_device.h"
 #include "tlsl_internal.h"
 #include "topk_common.h"
@@ -30,7 +32,7 @@ constexpr int TF_CHUNK = TF_NT * TF_PER;
 constexpr int TFIN_NT = 1024;           // final workgroup
 constexpr int TSEL_CAPMAX = 8448;       // candidate buffer entries per row, max
 constexpr int TSEL_BITMAP_WORDS = 4096; // rows up to 131072 use the bitmap output
-constexpr int TSEL_CNT_STRIDE = 32;   // one 128-byte line per row counter
+constexpr int TSEL_CNT_STRIDE = kTopkCntStride;  // one 128-byte line per row counter
 constexpr float TSEL_SIGMA = 4.0f;
 
 struct TopkArgs {
@@ -105,45 +107,49 @@ __global__ __launch_bounds__(TT_NT) void topk_threshold_kernel(TopkArgs a) {
 __global__ __launch_bounds__(TF_NT) void topk_filter_kernel(TopkArgs a) {
     const int r = blockIdx.y;
     const int L = max(a.row_len[r], 0);
-    const int base = blockIdx.x * TF_CHUNK;
-    if (base >= L) return;
     __shared__ int wsum[TF_NT / 64 + 1];
     const float th = a.theta[r];
     const float* sc = a.scores + a.row_start[r];
     uint2* out = a.buf + (size_t)r * a.cap;
     const int w = threadIdx.x >> 6;
-    float v[TF_PER];
+    // chunks blockIdx.x, + gridDim.x, ...: a row longer than the launch was
+    // sized for (max_len) is still filtered in full
+    for (int64_t base64 = (int64_t)blockIdx.x * TF_CHUNK; base64 < L; base64 += (int64_t)gridDim.x * TF_CHUNK) {
+        const int base = (int)base64;  // idx below stays < L + TF_CHUNK; rows hold < 2^31 - TF_CHUNK scores
+        float v[TF_PER];
 #pragma unroll
-    for (int i = 0; i < TF_PER; ++i) {
-        const int idx = base + i * TF_NT + threadIdx.x;
-        v[i] = idx < L ? sc[idx] : -INFINITY;
-    }
-    // count first, then reserve the workgroup's slots with a single atomic
-    uint64_t m[TF_PER];
-    int mine = 0;
+        for (int i = 0; i < TF_PER; ++i) {
+            const int idx = base + i * TF_NT + threadIdx.x;
+            v[i] = idx < L ? sc[idx] : -INFINITY;
+        }
+        // count first, then reserve the workgroup's slots with a single atomic
+        uint64_t m[TF_PER];
+        int mine = 0;
 #pragma unroll
-    for (int i = 0; i < TF_PER; ++i) {
-        const int idx = base + i * TF_NT + threadIdx.x;
-        m[i] = ballot(idx < L && v[i] >= th);
-        mine += __popcll(m[i]);
-    }
-    if (lane_id() == 0) wsum[w] = mine;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int tot = 0;
-        for (int i = 0; i < TF_NT / 64; ++i) tot += wsum[i];
-        wsum[TF_NT / 64] = tot > 0 ? atomicAdd(&a.cnt[r * TSEL_CNT_STRIDE], tot) : 0;
-    }
-    __syncthreads();
-    int slot = wsum[TF_NT / 64];
-    for (int i = 0; i < w; ++i) slot += wsum[i];
+        for (int i = 0; i < TF_PER; ++i) {
+            const int idx = base + i * TF_NT + threadIdx.x;
+            m[i] = ballot(idx < L && v[i] >= th);
+            mine += __popcll(m[i]);
+        }
+        if (lane_id() == 0) wsum[w] = mine;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int tot = 0;
+            for (int i = 0; i < TF_NT / 64; ++i) tot += wsum[i];
+            wsum[TF_NT / 64] = tot > 0 ? atomicAdd(&a.cnt[r * TSEL_CNT_STRIDE], tot) : 0;
+        }
+        __syncthreads();
+        int slot = wsum[TF_NT / 64];
+        for (int i = 0; i < w; ++i) slot += wsum[i];
 #pragma unroll
-    for (int i = 0; i < TF_PER; ++i) {
-        const int idx = base + i * TF_NT + threadIdx.x;
-        const bool ok = (m[i] >> lane_id()) & 1ull;
-        const int s = slot + rank_below(m[i]);
-        if (ok && s < a.cap) out[s] = make_uint2(__float_as_uint(v[i]), (uint32_t)idx);
-        slot += __popcll(m[i]);
+        for (int i = 0; i < TF_PER; ++i) {
+            const int idx = base + i * TF_NT + threadIdx.x;
+            const bool ok = (m[i] >> lane_id()) & 1ull;
+            const int s = slot + rank_below(m[i]);
+            if (ok && s < a.cap) out[s] = make_uint2(__float_as_uint(v[i]), (uint32_t)idx);
+            slot += __popcll(m[i]);
+        }
+        __syncthreads();  // wsum is reused by the next chunk
     }
 }
 
@@ -237,14 +243,6 @@ __global__ __launch_bounds__(TFIN_NT) void topk_final_kernel(TopkArgs a) {
     }
 }
 
-static int topk_cap(int k) { return (int)((2 * (size_t)k + 256 + 255) / 256 * 256); }
-
-static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-size_t topk_ws_bytes(int R, int k, int) {
-    return a256((size_t)R * sizeof(float)) + a256((size_t)R * TSEL_CNT_STRIDE * sizeof(int)) + a256((size_t)R * topk_cap(k) * sizeof(uint2));
-}
-
 hipError_t launch_topk_select(const float* scores, const int64_t* row_start, const int32_t* row_len, int R, int k,
                               int max_len, int32_t* S, float* S_score, void* ws, hipStream_t st) {
     unsigned char* w = static_cast<unsigned char*>(ws);
@@ -253,14 +251,15 @@ hipError_t launch_topk_select(const float* scores, const int64_t* row_start, con
     a.row_start = row_start;
     a.row_len = row_len;
     a.k = k;
-    a.cap = topk_cap(k);
-    a.theta = reinterpret_cast<float*>(w);
-    a.cnt = reinterpret_cast<int*>(w + a256((size_t)R * sizeof(float)));
-    a.buf = reinterpret_cast<uint2*>(w + a256((size_t)R * sizeof(float)) + a256((size_t)R * TSEL_CNT_STRIDE * sizeof(int)));
+    const TopkLayout lay = topk_layout(R, k);
+    a.cap = lay.cap;
+    a.theta = reinterpret_cast<float*>(w + lay.off_theta);
+    a.cnt = reinterpret_cast<int*>(w + lay.off_cnt);
+    a.buf = reinterpret_cast<uint2*>(w + lay.off_buf);
     a.S = S;
     a.Ss = S_score;
     TLSL_TIMED_LAUNCH("topk_threshold_kernel", st, hipLaunchKernelGGL(topk_threshold_kernel, dim3(R), dim3(TT_NT), 0, st, a));
-    const int chunks = max_len > 0 ? (max_len + TF_CHUNK - 1) / TF_CHUNK : 1;
+    const int chunks = max_len > 0 ? std::min((max_len + TF_CHUNK - 1) / TF_CHUNK, 65535) : 1;
     TLSL_TIMED_LAUNCH("topk_filter_kernel", st,
                       hipLaunchKernelGGL(topk_filter_kernel, dim3(chunks, R), dim3(TF_NT), 0, st, a));
     TLSL_TIMED_LAUNCH("topk_final_kernel", st, hipLaunchKernelGGL(topk_final_kernel, dim3(R), dim3(TFIN_NT), 0, st, a));
