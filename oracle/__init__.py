@@ -56,6 +56,7 @@ def _load():
         lib.ora_sparse_attn_decode.argtypes = [I, P, P, P, P, I, I, I, I, I, ctypes.c_double,
                                                P, I, P, P]
         lib.ora_sparse_attn_rows.argtypes = [I, P, P, P, P, I, I, I, I, I, ctypes.c_double, P, P]
+        lib.ora_indexer_kl.argtypes = [I, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P]
         lib.ora_num_threads.restype = I
         _lib = lib
     return _lib
@@ -212,3 +213,33 @@ def sparse_attn_rows(dt, q_rows, kv, S_rows, limits, scale, Dv):
     _check(lib.ora_sparse_attn_rows(dt, _ptr(q_rows), _ptr(kv), _ptr(S_rows), _ptr(limits), R, H, Dqk,
                                     Dv, k, float(scale), _ptr(out), _ptr(lse)), "sparse_attn_rows")
     return out, lse
+
+
+def indexer_kl(dt, q, q_scale, k_in, k_scale, w, S, p):
+    """Sparse-stage indexer loss (DSA page section 1.2 eq.(8), both sides
+    normalised over S_t) and its gradient, for every row of a batch.
+
+    q [B,n,HI,DI], k_in [B,n,DI] storage arrays, scales [B,n] or None,
+    w [B,n,HI] f32, S [B,n,k] int32 (slots outside [0,t] are not selected),
+    p [B,n,k] f32 teacher masses per slot (normalised over the valid slots).
+    Returns (loss [B,n], dq [B,n,HI,DI], dk [B,n,DI], dw [B,n,HI]), float64.
+    """
+    lib = _load()
+    q = _c(q)
+    k_in = _c(k_in)
+    w = _c(w, np.float32)
+    q_scale = _c(q_scale, np.float32)
+    k_scale = _c(k_scale, np.float32)
+    S = _c(S, np.int32)
+    p = _c(p, np.float32)
+    B, n, HI, DI = q.shape
+    k = S.shape[-1]
+    if S.shape != (B, n, k) or p.shape != (B, n, k) or k_in.shape != (B, n, DI) or w.shape != (B, n, HI):
+        raise ValueError("oracle indexer_kl: inconsistent shapes")
+    loss = np.empty((B, n), np.float64)
+    dq = np.empty((B, n, HI, DI), np.float64)
+    dk = np.empty((B, n, DI), np.float64)
+    dw = np.empty((B, n, HI), np.float64)
+    _check(lib.ora_indexer_kl(dt, _ptr(q), _ptr(q_scale), _ptr(k_in), _ptr(k_scale), _ptr(w), B, n, HI, DI, k,
+                              _ptr(S), _ptr(p), _ptr(loss), _ptr(dq), _ptr(dk), _ptr(dw)), "indexer_kl")
+    return loss, dq, dk, dw

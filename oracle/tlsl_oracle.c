@@ -409,6 +409,155 @@ int ora_sparse_attn_rows(int dt, const void *q_rows, const void *kv, const int32
     return 0;
 }
 
+/* ---- eq.(8): sparse-stage indexer loss and its gradient ------------------
+ *
+ * DSA page, section 1.2 eq.(8) and the normalisation rule after it: the
+ * indexer's loss on query t is KL(p_{t,S_t} || Softmax(I_{t,S_t})), both
+ * distributions normalised over the selected set S_t; a teacher sub-vector cut
+ * from a dense distribution is divided by its kept mass.  The indexer inputs
+ * are leaves (detached), so the gradient flows into q^I, k^I and w^I only.
+ *
+ * For row t with slots S[t, 0..k) (a slot outside [0, t] is not part of S_t)
+ * and teacher masses p[t, 0..k) (>= 0, normalised here over the valid slots):
+ *   I_i = sum_j w_j ReLU(q_j . k_{S_i})                   eq.(1)
+ *   P_i = p_i / sum_valid p                               kept-mass rule
+ *   R_i = exp(I_i) / sum_valid exp(I)                     Softmax(I_{t,S_t})
+ *   L_t = sum_valid P_i (log P_i - log R_i),  0 log 0 = 0  eq.(8)
+ * and with g_i = R_i - P_i (dL_t/dI_i) and ReLU'(x) = [x > 0]:
+ *   dL/dw_j  = sum_i g_i ReLU(q_j . k_{S_i})
+ *   dL/dq_j  = sum_i g_i w_j [q_j . k_{S_i} > 0] k_{S_i}
+ *   dL/dk_s += sum_{i: S_i = s} g_i sum_j w_j [q_j . k_s > 0] q_j
+ * summed over the rows for dk.  A row with no valid slot, or whose teacher
+ * has no mass on its valid slots, has L_t = 0 and no gradient.  Gradients
+ * are with respect to the dequantised values (for fp8, q = scale * code).
+ * All rows of the batch are computed; dk is accumulated in row order inside
+ * each thread's block of rows, the blocks summed in thread order. */
+int ora_indexer_kl(int dt, const void *qI, const float *q_scale, const void *kI,
+                   const float *k_scale, const float *wI, int B, int n, int HI, int DI, int k,
+                   const int32_t *S, const float *p, double *loss, double *dq, double *dk,
+                   double *dw)
+{
+    if (!qI || !kI || !wI || !S || !p || !loss || !dq || !dk || !dw || B <= 0 || n <= 0 ||
+        HI <= 0 || DI <= 0 || k <= 0)
+        return -1;
+    if (dt == ORA_FP8 && (!q_scale || !k_scale))
+        return -1;
+    const int64_t rows = (int64_t)B * n;
+    int nth = 1;
+#ifdef _OPENMP
+    nth = omp_get_max_threads();
+#endif
+    double *dk_part = calloc((size_t)nth * rows * DI, sizeof(double));
+    if (!dk_part)
+        return -1;
+#pragma omp parallel num_threads(nth)
+    {
+        int tid = 0;
+#ifdef _OPENMP
+        tid = omp_get_thread_num();
+#endif
+        double *mydk = dk_part + (size_t)tid * rows * DI;
+        double *q = malloc(sizeof(double) * (size_t)HI * DI);
+        double *w = malloc(sizeof(double) * (size_t)HI);
+        double *keys = malloc(sizeof(double) * (size_t)k * DI);
+        double *X = malloc(sizeof(double) * (size_t)k * HI);
+        double *I = malloc(sizeof(double) * (size_t)k);
+        double *g = malloc(sizeof(double) * (size_t)k);
+        int *valid = malloc(sizeof(int) * (size_t)k);
+#pragma omp for schedule(static)
+        for (int64_t row = 0; row < rows; ++row) {
+            int64_t b = row / n, t = row % n;
+            double *dqr = dq + row * HI * DI, *dwr = dw + row * HI;
+            for (int64_t i = 0; i < (int64_t)HI * DI; ++i)
+                dqr[i] = 0.0;
+            for (int j = 0; j < HI; ++j)
+                dwr[j] = 0.0;
+            loss[row] = 0.0;
+            const int32_t *Sr = S + row * k;
+            const float *pr = p + row * k;
+            load_token(dt, qI, q_scale, row, (int64_t)HI * DI, q);
+            for (int j = 0; j < HI; ++j)
+                w[j] = (double)wI[row * HI + j];
+            /* eq.(1) on the valid slots, keeping every q_j . k dot product */
+            double pmass = 0.0, imax = -INFINITY;
+            int nvalid = 0;
+            for (int i = 0; i < k; ++i) {
+                valid[i] = Sr[i] >= 0 && Sr[i] <= t;
+                if (!valid[i])
+                    continue;
+                ++nvalid;
+                load_token(dt, kI, k_scale, b * n + Sr[i], DI, keys + (int64_t)i * DI);
+                double sc = 0.0;
+                for (int j = 0; j < HI; ++j) {
+                    double dot = 0.0;
+                    for (int d = 0; d < DI; ++d)
+                        dot += q[(int64_t)j * DI + d] * keys[(int64_t)i * DI + d];
+                    X[(int64_t)i * HI + j] = dot;
+                    sc += w[j] * (dot > 0.0 ? dot : 0.0);
+                }
+                I[i] = sc;
+                pmass += (double)pr[i];
+                if (sc > imax)
+                    imax = sc;
+            }
+            if (nvalid == 0 || !(pmass > 0.0))
+                continue;
+            /* both distributions normalised over the valid slots */
+            double z = 0.0;
+            for (int i = 0; i < k; ++i)
+                if (valid[i])
+                    z += exp(I[i] - imax);
+            const double logz = imax + log(z);
+            double L = 0.0;
+            for (int i = 0; i < k; ++i) {
+                if (!valid[i]) {
+                    g[i] = 0.0;
+                    continue;
+                }
+                const double P = (double)pr[i] / pmass;
+                const double logR = I[i] - logz;
+                if (P > 0.0)
+                    L += P * (log(P) - logR);
+                g[i] = exp(logR) - P;
+            }
+            loss[row] = L;
+            /* the chain rule through eq.(1) */
+            for (int i = 0; i < k; ++i) {
+                if (!valid[i])
+                    continue;
+                const double *ki = keys + (int64_t)i * DI;
+                double *dks = mydk + (b * n + Sr[i]) * DI;
+                for (int j = 0; j < HI; ++j) {
+                    const double x = X[(int64_t)i * HI + j];
+                    dwr[j] += g[i] * (x > 0.0 ? x : 0.0);
+                    if (!(x > 0.0))
+                        continue;
+                    const double c = g[i] * w[j];
+                    for (int d = 0; d < DI; ++d) {
+                        dqr[(int64_t)j * DI + d] += c * ki[d];
+                        dks[d] += c * q[(int64_t)j * DI + d];
+                    }
+                }
+            }
+        }
+        free(q);
+        free(w);
+        free(keys);
+        free(X);
+        free(I);
+        free(g);
+        free(valid);
+    }
+    for (int64_t i = 0; i < rows * DI; ++i) {
+        double acc = 0.0;
+        for (int th = 0; th < nth; ++th)
+            acc += dk_part[(size_t)th * rows * DI + i];
+        dk[i] = acc;
+    }
+    free(dk_part);
+    return 0;
+}
+
 int ora_num_threads(void)
 {
     int n = 1;
