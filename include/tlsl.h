@@ -142,6 +142,26 @@ int topk_select(const float* scores, const int64_t* row_start, const int32_t* ro
                 size_t* ws_bytes, hipStream_t stream);
 
 /*
+ * topk_select_noalloc -- topk_select for callers that cannot allocate memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the workspace taken from a
+ * fixed device array inside the library instead of a caller's buffer.  The
+ * call itself allocates nothing and clears nothing (every scratch byte it
+ * reads is written earlier in the same call).
+ *
+ * Arguments as topk_select.  The scratch array holds TLSL_NOALLOC_SCRATCH_BYTES
+ * bytes on each device the library runs on, from the first call on that device
+ * until the process ends; a problem needing more (topk_select's queried
+ * workspace size, about R*(2k+264)*8 bytes, e.g. more than ~480 rows at
+ * k = 2048) returns TLSL_ERR_WORKSPACE without launching.  Calls that overlap
+ * on one device (two streams, two threads) share the array and race: the
+ * caller orders them.
+ */
+#define TLSL_NOALLOC_SCRATCH_BYTES (16u << 20)
+int topk_select_noalloc(const float* scores, const int64_t* row_start, const int32_t* row_len, int R,
+                        int k, int max_len, int32_t* S, float* S_score, hipStream_t stream);
+
+/*
  * sparse_attn_prefill -- attention of every query over its selected shared
  * latent entries (DSA page, section 1.1 eq.(3); the Sparse MLA paragraph after
  * eq.(1) gathers the latent KV named by S[t,:]).  For query (b,t), head h and

@@ -72,6 +72,13 @@ int main() {
     EXPECT(topk_select(static_cast<float*>(reinterpret_cast<void*>(uintptr_t(0x10002))), I64, I32, 64, 2048, 10, I32,
                        F, nullptr, &need, nullptr), TLSL_ERR_ALIGN);
 
+    // ---- topk_select_noalloc: the same checks, a fixed scratch instead of a workspace
+    EXPECT(topk_select_noalloc(F, I64, I32, 64, 2048, 131072, I32, F, nullptr), TLSL_OK);
+    EXPECT(topk_select_noalloc(F, I64, I32, 481, 2048, 131072, I32, F, nullptr), TLSL_ERR_WORKSPACE);
+    EXPECT(topk_select_noalloc(F, I64, I32, 480, 2048, 131072, I32, F, nullptr), TLSL_OK);
+    EXPECT(topk_select_noalloc(nullptr, I64, I32, 64, 2048, 131072, I32, F, nullptr), TLSL_ERR_NULL);
+    EXPECT(topk_select_noalloc(F, I64, I32, 64, 4097, 131072, I32, F, nullptr), TLSL_ERR_UNSUPPORTED);
+
     // ---- attention
     const float sc = 0.05f;
     EXPECT(sparse_attn_prefill(P, P, I32, 1, 100, 128, 576, 512, 2048, sc, TLSL_BF16, P, F, nullptr, &ws, nullptr), TLSL_OK);
@@ -92,10 +99,11 @@ int main() {
     EXPECT(sparse_attn_decode(P, P, I64, I32, 64, 128, 576, 512, 2048, sc, TLSL_BF16, P, F, nullptr, nullptr, nullptr), TLSL_ERR_NULL);
     if (strlen(tlsl_version()) == 0) ++g_fail;
 
-    // accepted calls: index_prefill, index_decode, topk_select, sparse_attn_prefill,
-    // dense_attn_prefill, sparse_attn_decode (the last one's stand-in fails on purpose)
-    if (g_launches != 6) {
-        fprintf(stderr, "expected 6 launches, saw %d\n", g_launches);
+    // accepted calls: index_prefill, index_decode, topk_select, topk_select_noalloc (2),
+    // sparse_attn_prefill, dense_attn_prefill, sparse_attn_decode (the last one's
+    // stand-in fails on purpose)
+    if (g_launches != 8) {
+        fprintf(stderr, "expected 8 launches, saw %d\n", g_launches);
         ++g_fail;
     }
     if (g_fail) return 1;

@@ -3,6 +3,7 @@
 // address and undefined-behaviour sanitizers and driven without a GPU.  Each
 // launcher records that it was reached and returns hipSuccess; nothing is
 // dereferenced.  TEST INFRASTRUCTURE ONLY.
+#include <stdint.h>
 #include <stdio.h>
 
 #include "../../token_level_sparse_lightning_amd/csrc/tlsl_internal.h"
@@ -23,6 +24,10 @@ hipError_t launch_index_prefill(const IndexerShape&, const void*, const float*, 
 hipError_t launch_index_decode(const IndexerShape&, const void*, const float*, const void*, const float*,
                                const float*, const int64_t*, int, int, float*, hipStream_t) {
     ++g_launches;
+    return hipSuccess;
+}
+hipError_t topk_noalloc_scratch(void** out) {
+    *out = reinterpret_cast<void*>(uintptr_t(0x20000));
     return hipSuccess;
 }
 hipError_t launch_topk_select(const float*, const int64_t*, const int32_t*, int, int, int, int32_t*, float*, void*,

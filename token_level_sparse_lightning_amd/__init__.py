@@ -21,5 +21,6 @@ from .binding import (  # noqa: F401
     timer_arm,
     timer_collect,
     topk_select,
+    topk_select_noalloc,
     topk_select_workspace_bytes,
 )

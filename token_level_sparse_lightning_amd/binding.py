@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libtlsl.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 
-EXPORTS = ("index_prefill", "index_decode", "topk_select", "sparse_attn_prefill",
+EXPORTS = ("index_prefill", "index_decode", "topk_select", "topk_select_noalloc", "sparse_attn_prefill",
            "dense_attn_prefill", "sparse_attn_decode", "tlsl_last_error", "tlsl_version",
            # measurement aids (include/tlsl_measure.h)
            "tlsl_timer_arm", "tlsl_timer_collect", "tlsl_calib_copy", "tlsl_calib_mfma")
@@ -45,10 +45,12 @@ def load():
     lib.index_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, P, SZ, P]
     lib.index_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, SZ, P]
     lib.topk_select.argtypes = [P, P, P, I, I, I, P, P, P, SZ, P]
+    lib.topk_select_noalloc.argtypes = [P, P, P, I, I, I, P, P, P]
     lib.sparse_attn_prefill.argtypes = [P, P, P, I, I, I, I, I, I, F, I, P, P, P, SZ, P]
     lib.dense_attn_prefill.argtypes = [P, P, I, I, I, I, I, F, I, P, P, P, SZ, P]
     lib.sparse_attn_decode.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, P, P, SZ, P]
-    for fn in ("index_prefill", "index_decode", "topk_select", "sparse_attn_prefill", "dense_attn_prefill",
+    for fn in ("index_prefill", "index_decode", "topk_select", "topk_select_noalloc", "sparse_attn_prefill",
+               "dense_attn_prefill",
                "sparse_attn_decode"):
         getattr(lib, fn).restype = I
     lib.tlsl_last_error.restype = ctypes.c_char_p
@@ -171,6 +173,22 @@ def topk_select(scores, row_start, row_len, k, max_len, S=None, S_score=None, wa
     rc = lib.topk_select(_ptr(scores), _ptr(row_start), _ptr(row_len), R, k, int(max_len), _ptr(S),
                          _ptr(S_score), _ptr(workspace), ctypes.byref(size), _stream(stream))
     _check("topk_select", rc)
+    return S, S_score
+
+
+def topk_select_noalloc(scores, row_start, row_len, k, max_len, S=None, S_score=None, want_scores=False,
+                        stream=None):
+    """topk_select with the library's fixed device scratch instead of a
+    workspace (the call allocates nothing; the outputs are the caller's)."""
+    lib = load()
+    R = row_len.shape[0]
+    if S is None:
+        S = torch.empty((R, k), dtype=torch.int32, device=scores.device)
+    if S_score is None and want_scores:
+        S_score = torch.empty((R, k), dtype=torch.float32, device=scores.device)
+    rc = lib.topk_select_noalloc(_ptr(scores), _ptr(row_start), _ptr(row_len), R, k, int(max_len), _ptr(S),
+                                 _ptr(S_score), _stream(stream))
+    _check("topk_select_noalloc", rc)
     return S, S_score
 
 

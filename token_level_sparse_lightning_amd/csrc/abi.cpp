@@ -72,6 +72,19 @@ int check_indexer(int dt, const void* q, const float* q_scale, const void* k, co
     return 0;
 }
 
+int check_topk(const float* scores, const int64_t* row_start, const int32_t* row_len, int R, int k, int max_len,
+               const int32_t* S, const float* S_score, const char* fn) {
+    if (!scores || !row_start || !row_len || !S) return fail(TLSL_ERR_NULL, "%s: NULL pointer argument", fn);
+    if (R <= 0) return fail(TLSL_ERR_SHAPE, "%s: R=%d must be positive", fn, R);
+    if (k <= 0) return fail(TLSL_ERR_SHAPE, "%s: k=%d must be positive", fn, k);
+    if (k > 4096) return fail(TLSL_ERR_UNSUPPORTED, "%s: k=%d above the supported 4096", fn, k);
+    if (max_len < 0) return fail(TLSL_ERR_SHAPE, "%s: max_len=%d must be >= 0", fn, max_len);
+    if (!aligned16(S) || !aligned16(S_score) || !aligned16(row_start) || !aligned16(row_len))
+        return fail(TLSL_ERR_ALIGN, "%s: pointers not 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(scores) & 3u) != 0) return fail(TLSL_ERR_ALIGN, "%s: scores not 4-byte aligned", fn);
+    return 0;
+}
+
 }  // namespace
 
 int tlsl::report(int code, const char* fmt, ...) {
@@ -131,19 +144,31 @@ int index_decode(const void* qI, const float* q_scale, const void* kI_cache, con
 
 int topk_select(const float* scores, const int64_t* row_start, const int32_t* row_len, int R, int k, int max_len,
                 int32_t* S, float* S_score, void* workspace, size_t* ws_bytes, hipStream_t stream) {
-    if (!scores || !row_start || !row_len || !S) return fail(TLSL_ERR_NULL, "topk_select: NULL pointer argument");
-    if (R <= 0) return fail(TLSL_ERR_SHAPE, "topk_select: R=%d must be positive", R);
-    if (k <= 0) return fail(TLSL_ERR_SHAPE, "topk_select: k=%d must be positive", k);
-    if (k > 4096) return fail(TLSL_ERR_UNSUPPORTED, "topk_select: k=%d above the supported 4096", k);
-    if (max_len < 0) return fail(TLSL_ERR_SHAPE, "topk_select: max_len=%d must be >= 0", max_len);
-    if (!aligned16(S) || !aligned16(S_score) || !aligned16(row_start) || !aligned16(row_len))
-        return fail(TLSL_ERR_ALIGN, "topk_select: pointers not 16-byte aligned");
-    if ((reinterpret_cast<uintptr_t>(scores) & 3u) != 0) return fail(TLSL_ERR_ALIGN, "topk_select: scores not 4-byte aligned");
-    const int rc = workspace_protocol(workspace, ws_bytes, tlsl::topk_ws_bytes(R, k, max_len));
+    int rc = check_topk(scores, row_start, row_len, R, k, max_len, S, S_score, "topk_select");
+    if (rc) return rc;
+    rc = workspace_protocol(workspace, ws_bytes, tlsl::topk_ws_bytes(R, k, max_len));
     if (rc) return rc > 0 ? ok() : rc;
     return launch_result(tlsl::launch_topk_select(scores, row_start, row_len, R, k, max_len, S, S_score, workspace,
                                                   stream),
                          "topk_select");
+}
+
+int topk_select_noalloc(const float* scores, const int64_t* row_start, const int32_t* row_len, int R, int k,
+                        int max_len, int32_t* S, float* S_score, hipStream_t stream) {
+    const int rc = check_topk(scores, row_start, row_len, R, k, max_len, S, S_score, "topk_select_noalloc");
+    if (rc) return rc;
+    const size_t need = tlsl::topk_ws_bytes(R, k, max_len);
+    if (need > (size_t)TLSL_NOALLOC_SCRATCH_BYTES)
+        return fail(TLSL_ERR_WORKSPACE,
+                    "topk_select_noalloc: R=%d rows at k=%d need %zu bytes of scratch, above its fixed %zu "
+                    "(call topk_select with a workspace instead)",
+                    R, k, need, (size_t)TLSL_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    const hipError_t e = tlsl::topk_noalloc_scratch(&ws);
+    if (e != hipSuccess)
+        return fail(TLSL_ERR_HIP, "topk_select_noalloc: device address of the scratch array: %s", hipGetErrorString(e));
+    return launch_result(tlsl::launch_topk_select(scores, row_start, row_len, R, k, max_len, S, S_score, ws, stream),
+                         "topk_select_noalloc");
 }
 
 int sparse_attn_prefill(const void* q, const void* kv, const int32_t* S, int B, int n, int H, int Dqk, int Dv, int k,

@@ -61,6 +61,9 @@ struct TopkLayout {
 };
 TopkLayout topk_layout(int R, int k);
 size_t topk_ws_bytes(int R, int k, int max_len);
+// device address of the allocation-free variant's scratch array on the
+// current device (TLSL_NOALLOC_SCRATCH_BYTES bytes)
+hipError_t topk_noalloc_scratch(void** out);
 hipError_t launch_topk_select(const float* scores, const int64_t* row_start,
                               const int32_t* row_len, int R, int k, int max_len, int32_t* S,
                               float* S_score, void* ws, hipStream_t st);

@@ -17,7 +17,9 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
+#include "../../include/tlsl.h"
 #include "tlsl_device.h"
 #include "tlsl_internal.h"
 #include "topk_common.h"
@@ -264,6 +266,36 @@ hipError_t launch_topk_select(const float* scores, const int64_t* row_start, con
                       hipLaunchKernelGGL(topk_filter_kernel, dim3(chunks, R), dim3(TF_NT), 0, st, a));
     TLSL_TIMED_LAUNCH("topk_final_kernel", st, hipLaunchKernelGGL(topk_final_kernel, dim3(R), dim3(TFIN_NT), 0, st, a));
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant: topk_select_noalloc runs the same three kernels
+// with their workspace in this file-scope device array (one per device, held
+// until the process ends).  Every byte of it that the kernels read is written
+// earlier in the same call (the threshold kernel sets each row's threshold
+// and zeroes its counter, the filter fills the candidate buffers up to that
+// counter), so nothing needs clearing between calls; calls that overlap on
+// one device share the array and race.  Host code never uses the array's name
+// as an address: it takes the device address with hipGetSymbolAddress, once
+// per device with that device current, and passes that pointer.
+static __device__ __align__(256) unsigned char scratch[TLSL_NOALLOC_SCRATCH_BYTES];
+
+hipError_t topk_noalloc_scratch(void** out) {
+    static std::mutex mu;
+    static void* addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace tlsl
