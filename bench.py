@@ -17,6 +17,8 @@ other rows of the path, each on its own workload (``extra``):
   decode               one decode step of 64 ragged sequences
                        (L ~ U[16384,131072]): index_decode + topk_select +
                        sparse_attn_decode, tokens/s
+  train_8192           indexer_loss_grad (the eq.(8) training step: loss and
+                       gradient) over index_prefill's selection, n=8192, bf16
   tiny_f32_512         index_prefill + sparse_attn_prefill on B=1, n=512,
                        H^I=4, d^I=32, k=64, fp32 (report only: launch-bound)
 
@@ -198,6 +200,39 @@ def bench_attn_dense(n, seed, steps, warmup):
     return dict(workload=f"dense (short) attention prefill: n={n}, H={H}, Dqk={Dqk}, Dv={Dv}, bf16",
                 causal_pairs=pairs, flops_per_call=flops, kernel="sparse_attn_kernel", kernel_tflops=ach,
                 peak_tflops=PEAK_BF16_TFLOPS, frac=ach / PEAK_BF16_TFLOPS, **tm.as_dict())
+
+
+def bench_train(seed, steps, warmup):
+    """The indexer's sparse-stage training step (indexer_loss_grad) on the
+    n=8192 bf16 workload, over index_prefill's selection with a synthetic
+    teacher.  Unit: one selected (query, key) pair; algorithmic flops per pair
+    2*H^I*d^I each for the score, dq and dk contractions."""
+    n, HI, DI, k = 8192, 64, 128, 2048
+    log(f"train n={n}: generating inputs")
+    inp = synth.indexer_prefill(1, n, HI, DI, synth.DT_BF16, seed, planted=True, device=DEV)
+    S, _ = tl.index_prefill(inp.q, inp.k, inp.w, k)
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    p = torch.rand((1, n, k), generator=g, device=DEV) ** 3 + 1e-3
+    loss = torch.empty((1, n), dtype=torch.float32, device=DEV)
+    dq = torch.empty((1, n, HI, DI), dtype=torch.float32, device=DEV)
+    dk = torch.empty((1, n, DI), dtype=torch.float32, device=DEV)
+    dw = torch.empty((1, n, HI), dtype=torch.float32, device=DEV)
+
+    def call():
+        tl.indexer_loss_grad(inp.q, inp.k, inp.w, S, p, loss=loss, dq=dq, dk=dk, dw=dw)
+
+    tm = time_calls(call, steps, warmup, kernel="indexer_kl_kernel")
+    pairs = int((S >= 0).sum().item())
+    flops = 3 * 2.0 * HI * DI * pairs
+    ach = flops / (tm.kernel_avg * 1e-3) / 1e12
+    log(f"train: {tm.ev_med:.3f} ms/call (events, median), indexer_kl_kernel {tm.kernel_avg:.3f} ms, "
+        f"{pairs / (tm.ev_med * 1e-3):.3g} pairs/s, {ach:.1f} TFLOP/s")
+    del inp, S, p, dq, dk, dw
+    return dict(workload=f"indexer training step (eq.(8) loss and gradient): B=1, n={n}, H^I={HI}, d^I={DI}, "
+                         f"k={k}, bf16, index_prefill's selection, synthetic teacher",
+                selected_pairs=pairs, pairs_per_s=pairs / (tm.wall * 1e-3), flops_per_call=flops,
+                kernel="indexer_kl_kernel", kernel_tflops=ach, peak_tflops=PEAK_BF16_TFLOPS,
+                frac=ach / PEAK_BF16_TFLOPS, **tm.as_dict())
 
 
 def bench_tiny(steps, warmup):
@@ -394,7 +429,7 @@ def recorded_traffic(kernel, workload):
 
 
 EXTRAS = ("attn_prefill_131072", "prefill_bf16_8192", "prefill_fp8_32768", "attn_prefill_32768",
-          "attn_dense_2048", "decode", "tiny_f32_512")
+          "attn_dense_2048", "decode", "train_8192", "tiny_f32_512")
 
 
 def main():
@@ -449,6 +484,9 @@ def main():
         torch.cuda.empty_cache()
     if "decode" in want:
         extra["decode"] = bench_decode(4, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+    if "train_8192" in want:
+        extra["train_8192"] = bench_train(2, max(5, args.steps // 2), 2)
         torch.cuda.empty_cache()
     if "tiny_f32_512" in want:
         extra["tiny_f32_512"] = bench_tiny(args.steps, args.warmup)

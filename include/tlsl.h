@@ -36,7 +36,8 @@
  *    written in ascending position order, followed by -1 in the unused slots.
  *    Ties in the score go to the lower position; -0.0 equals +0.0.  NaN or
  *    infinite inputs are not supported.
- *  - Results are bitwise reproducible for identical inputs and shapes.
+ *  - Results are bitwise reproducible for identical inputs and shapes (the
+ *    one exception, indexer_loss_grad's dk, says so below).
  *  - fp8 means OCP e4m3 (e4m3fn: bias 7, max 448, no infinities), the format
  *    gfx950's matrix cores take, with one fp32 scale per token: a value is
  *    scale * code.  Scales must be finite and > 0: the kernels take them out
@@ -160,6 +161,38 @@ int topk_select(const float* scores, const int64_t* row_start, const int32_t* ro
 #define TLSL_NOALLOC_SCRATCH_BYTES (16u << 20)
 int topk_select_noalloc(const float* scores, const int64_t* row_start, const int32_t* row_len, int R,
                         int k, int max_len, int32_t* S, float* S_score, hipStream_t stream);
+
+/*
+ * indexer_loss_grad -- one step of the indexer's sparse-stage training: the
+ * loss of the DSA page, section 1.2 eq.(8), and its gradient.  For every row
+ * (b, t) the valid slots i of S[b,t,:] (0 <= S[b,t,i] <= t) form S_t and
+ *     I_i  = sum_j w[b,t,j] * ReLU(q[b,t,j,:] . k[b,S[b,t,i],:])   (eq.(1))
+ *     P_i  = p[b,t,i] / sum_{valid} p[b,t,.]     (the teacher renormalised by
+ *            its kept mass, as the page requires after eq.(8))
+ *     R_i  = exp(I_i) / sum_{valid} exp(I)       (Softmax over S_t)
+ *     loss[b,t] = sum_{valid} P_i (log P_i - log R_i),   0 log 0 = 0.
+ * The indexer inputs are detached from the main model (section 1.2), so the
+ * gradient of sum_{b,t} loss[b,t] is taken with respect to them only, with
+ * ReLU'(0) = 0:
+ *     dq [B,n,HI,dI], dw [B,n,HI]: per row;
+ *     dk [B,n,dI]: summed over every query that selected the key (the call
+ *         overwrites dk; keys no query selected get 0).
+ * A row with no valid slot, or whose teacher has no mass on them, has loss 0
+ * and contributes no gradient.  S is typically index_prefill's output and p
+ * the main attention's probabilities on those slots summed over heads; any
+ * p >= 0 is accepted.
+ *
+ *   qI [B,n,HI,dI] bf16, kI [B,n,dI] bf16, wI [B,n,HI] fp32,
+ *   S [B,n,k] int32, p [B,n,k] fp32; outputs fp32.
+ * Supported: dt = BF16 with dI = 128, 1 <= HI <= 64, 1 <= k <= 4096,
+ * B*n <= 2^30.  Scores, softmax and products accumulate in fp32 (the
+ * coefficients of the backward products carry ~16 significant bits).  loss,
+ * dq and dw are bitwise reproducible; dk is accumulated with atomic adds, so
+ * its last bits may vary between runs.  Needs no workspace.
+ */
+int indexer_loss_grad(const void* qI, const void* kI, const float* wI, const int32_t* S,
+                      const float* p, int B, int n, int HI, int dI, int k, tlsl_dtype dt,
+                      float* loss, float* dq, float* dk, float* dw, hipStream_t stream);
 
 /*
  * sparse_attn_prefill -- attention of every query over its selected shared

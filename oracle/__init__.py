@@ -57,6 +57,7 @@ def _load():
                                                P, I, P, P]
         lib.ora_sparse_attn_rows.argtypes = [I, P, P, P, P, I, I, I, I, I, ctypes.c_double, P, P]
         lib.ora_indexer_kl.argtypes = [I, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P]
+        lib.ora_indexer_kl_mag.argtypes = [I, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.ora_num_threads.restype = I
         _lib = lib
     return _lib
@@ -215,14 +216,19 @@ def sparse_attn_rows(dt, q_rows, kv, S_rows, limits, scale, Dv):
     return out, lse
 
 
-def indexer_kl(dt, q, q_scale, k_in, k_scale, w, S, p):
+def indexer_kl(dt, q, q_scale, k_in, k_scale, w, S, p, want_mags=False):
     """Sparse-stage indexer loss (DSA page section 1.2 eq.(8), both sides
     normalised over S_t) and its gradient, for every row of a batch.
 
     q [B,n,HI,DI], k_in [B,n,DI] storage arrays, scales [B,n] or None,
     w [B,n,HI] f32, S [B,n,k] int32 (slots outside [0,t] are not selected),
     p [B,n,k] f32 teacher masses per slot (normalised over the valid slots).
-    Returns (loss [B,n], dq [B,n,HI,DI], dk [B,n,DI], dw [B,n,HI]), float64.
+    Returns (loss [B,n], dq [B,n,HI,DI], dk [B,n,DI], dw [B,n,HI]), float64;
+    with ``want_mags`` also their magnitude sums (the same shapes; the sums of
+    the terms' absolute values with |g_i| replaced by R_i + P_i) and the kink
+    bands of dq and dk (the terms whose dot product lies within fp32
+    accumulation rounding of ReLU's kink), which tests use to bound the
+    difference of a result computed in fp32.
     """
     lib = _load()
     q = _c(q)
@@ -240,6 +246,13 @@ def indexer_kl(dt, q, q_scale, k_in, k_scale, w, S, p):
     dq = np.empty((B, n, HI, DI), np.float64)
     dk = np.empty((B, n, DI), np.float64)
     dw = np.empty((B, n, HI), np.float64)
-    _check(lib.ora_indexer_kl(dt, _ptr(q), _ptr(q_scale), _ptr(k_in), _ptr(k_scale), _ptr(w), B, n, HI, DI, k,
-                              _ptr(S), _ptr(p), _ptr(loss), _ptr(dq), _ptr(dk), _ptr(dw)), "indexer_kl")
-    return loss, dq, dk, dw
+    if not want_mags:
+        _check(lib.ora_indexer_kl(dt, _ptr(q), _ptr(q_scale), _ptr(k_in), _ptr(k_scale), _ptr(w), B, n, HI, DI, k,
+                                  _ptr(S), _ptr(p), _ptr(loss), _ptr(dq), _ptr(dk), _ptr(dw)), "indexer_kl")
+        return loss, dq, dk, dw
+    mags = (np.empty_like(loss), np.empty_like(dq), np.empty_like(dk), np.empty_like(dw), np.empty_like(dq),
+            np.empty_like(dk))
+    _check(lib.ora_indexer_kl_mag(dt, _ptr(q), _ptr(q_scale), _ptr(k_in), _ptr(k_scale), _ptr(w), B, n, HI, DI, k,
+                                  _ptr(S), _ptr(p), _ptr(loss), _ptr(dq), _ptr(dk), _ptr(dw), *(_ptr(m) for m in mags)),
+           "indexer_kl")
+    return (loss, dq, dk, dw) + mags

@@ -432,10 +432,39 @@ int ora_sparse_attn_rows(int dt, const void *q_rows, const void *kv, const int32
  * are with respect to the dequantised values (for fp8, q = scale * code).
  * All rows of the batch are computed; dk is accumulated in row order inside
  * each thread's block of rows, the blocks summed in thread order. */
+/* Optional magnitude sums (NULL to skip), the sums of the absolute values of
+ * the terms, with |g_i| replaced by R_i + P_i, used by tests to scale the
+ * tolerance of a result computed in lower precision:
+ *   loss_mag = sum_valid P_i (|log P_i| + |log R_i|)
+ *   dq_mag   = sum_i (R_i + P_i) |w_j| [x > 0] |k_{S_i}|      (per j, d)
+ *   dk_mag  += sum_{i: S_i = s} (R_i + P_i) sum_j |w_j| [x > 0] |q_j|
+ *   dw_mag   = sum_i (R_i + P_i) ReLU(x)                     (per j)
+ * and the kink bands: the same dq and dk terms, at full weight, for every x =
+ * q_j . k_s within DI * 2^-24 * sum_d |q_jd k_sd| of zero -- there an fp32
+ * accumulation of the dot product (in any order) may land on either side of
+ * the ReLU's kink, so a result computed in fp32 may count the term or not:
+ *   dq_kink  = sum_{i: |x| <= band} (R_i + P_i) |w_j| |k_{S_i}|
+ *   dk_kink += sum_{i: S_i = s} (R_i + P_i) sum_{j: |x| <= band} |w_j| |q_j| */
+int ora_indexer_kl_mag(int dt, const void *qI, const float *q_scale, const void *kI,
+                       const float *k_scale, const float *wI, int B, int n, int HI, int DI, int k,
+                       const int32_t *S, const float *p, double *loss, double *dq, double *dk,
+                       double *dw, double *loss_mag, double *dq_mag, double *dk_mag,
+                       double *dw_mag, double *dq_kink, double *dk_kink);
+
 int ora_indexer_kl(int dt, const void *qI, const float *q_scale, const void *kI,
                    const float *k_scale, const float *wI, int B, int n, int HI, int DI, int k,
                    const int32_t *S, const float *p, double *loss, double *dq, double *dk,
                    double *dw)
+{
+    return ora_indexer_kl_mag(dt, qI, q_scale, kI, k_scale, wI, B, n, HI, DI, k, S, p, loss, dq, dk,
+                              dw, NULL, NULL, NULL, NULL, NULL, NULL);
+}
+
+int ora_indexer_kl_mag(int dt, const void *qI, const float *q_scale, const void *kI,
+                       const float *k_scale, const float *wI, int B, int n, int HI, int DI, int k,
+                       const int32_t *S, const float *p, double *loss, double *dq, double *dk,
+                       double *dw, double *loss_mag, double *dq_mag, double *dk_mag,
+                       double *dw_mag, double *dq_kink, double *dk_kink)
 {
     if (!qI || !kI || !wI || !S || !p || !loss || !dq || !dk || !dw || B <= 0 || n <= 0 ||
         HI <= 0 || DI <= 0 || k <= 0)
@@ -447,7 +476,8 @@ int ora_indexer_kl(int dt, const void *qI, const float *q_scale, const void *kI,
 #ifdef _OPENMP
     nth = omp_get_max_threads();
 #endif
-    double *dk_part = calloc((size_t)nth * rows * DI, sizeof(double));
+    const int want_mag = loss_mag && dq_mag && dk_mag && dw_mag && dq_kink && dk_kink;
+    double *dk_part = calloc((size_t)nth * rows * DI * (want_mag ? 3 : 1), sizeof(double));
     if (!dk_part)
         return -1;
 #pragma omp parallel num_threads(nth)
@@ -457,6 +487,10 @@ int ora_indexer_kl(int dt, const void *qI, const float *q_scale, const void *kI,
         tid = omp_get_thread_num();
 #endif
         double *mydk = dk_part + (size_t)tid * rows * DI;
+        double *mydkm = want_mag ? dk_part + ((size_t)nth + tid) * rows * DI : NULL;
+        double *mydkk = want_mag ? dk_part + ((size_t)2 * nth + tid) * rows * DI : NULL;
+        double *band = malloc(sizeof(double) * (size_t)k * HI);
+        double *R = malloc(sizeof(double) * (size_t)k), *Pn = malloc(sizeof(double) * (size_t)k);
         double *q = malloc(sizeof(double) * (size_t)HI * DI);
         double *w = malloc(sizeof(double) * (size_t)HI);
         double *keys = malloc(sizeof(double) * (size_t)k * DI);
@@ -473,6 +507,15 @@ int ora_indexer_kl(int dt, const void *qI, const float *q_scale, const void *kI,
             for (int j = 0; j < HI; ++j)
                 dwr[j] = 0.0;
             loss[row] = 0.0;
+            if (want_mag) {
+                loss_mag[row] = 0.0;
+                for (int64_t i = 0; i < (int64_t)HI * DI; ++i) {
+                    dq_mag[row * HI * DI + i] = 0.0;
+                    dq_kink[row * HI * DI + i] = 0.0;
+                }
+                for (int j = 0; j < HI; ++j)
+                    dw_mag[row * HI + j] = 0.0;
+            }
             const int32_t *Sr = S + row * k;
             const float *pr = p + row * k;
             load_token(dt, qI, q_scale, row, (int64_t)HI * DI, q);
@@ -489,10 +532,13 @@ int ora_indexer_kl(int dt, const void *qI, const float *q_scale, const void *kI,
                 load_token(dt, kI, k_scale, b * n + Sr[i], DI, keys + (int64_t)i * DI);
                 double sc = 0.0;
                 for (int j = 0; j < HI; ++j) {
-                    double dot = 0.0;
-                    for (int d = 0; d < DI; ++d)
+                    double dot = 0.0, adot = 0.0;
+                    for (int d = 0; d < DI; ++d) {
                         dot += q[(int64_t)j * DI + d] * keys[(int64_t)i * DI + d];
+                        adot += fabs(q[(int64_t)j * DI + d] * keys[(int64_t)i * DI + d]);
+                    }
                     X[(int64_t)i * HI + j] = dot;
+                    band[(int64_t)i * HI + j] = (double)DI * ldexp(1.0, -24) * adot;
                     sc += w[j] * (dot > 0.0 ? dot : 0.0);
                 }
                 I[i] = sc;
@@ -519,6 +565,10 @@ int ora_indexer_kl(int dt, const void *qI, const float *q_scale, const void *kI,
                 if (P > 0.0)
                     L += P * (log(P) - logR);
                 g[i] = exp(logR) - P;
+                R[i] = exp(logR);
+                Pn[i] = P;
+                if (want_mag && P > 0.0)
+                    loss_mag[row] += P * (fabs(log(P)) + fabs(logR));
             }
             loss[row] = L;
             /* the chain rule through eq.(1) */
@@ -530,12 +580,31 @@ int ora_indexer_kl(int dt, const void *qI, const float *q_scale, const void *kI,
                 for (int j = 0; j < HI; ++j) {
                     const double x = X[(int64_t)i * HI + j];
                     dwr[j] += g[i] * (x > 0.0 ? x : 0.0);
+                    if (want_mag) {
+                        dw_mag[row * HI + j] += (R[i] + Pn[i]) * (x > 0.0 ? x : 0.0);
+                        if (fabs(x) <= band[(int64_t)i * HI + j]) {
+                            const double cm = (R[i] + Pn[i]) * fabs(w[j]);
+                            double *dkk = mydkk + (b * n + Sr[i]) * DI;
+                            for (int d = 0; d < DI; ++d) {
+                                dq_kink[row * HI * DI + (int64_t)j * DI + d] += cm * fabs(ki[d]);
+                                dkk[d] += cm * fabs(q[(int64_t)j * DI + d]);
+                            }
+                        }
+                    }
                     if (!(x > 0.0))
                         continue;
                     const double c = g[i] * w[j];
                     for (int d = 0; d < DI; ++d) {
                         dqr[(int64_t)j * DI + d] += c * ki[d];
                         dks[d] += c * q[(int64_t)j * DI + d];
+                    }
+                    if (want_mag) {
+                        const double cm = (R[i] + Pn[i]) * fabs(w[j]);
+                        double *dkm = mydkm + (b * n + Sr[i]) * DI;
+                        for (int d = 0; d < DI; ++d) {
+                            dq_mag[row * HI * DI + (int64_t)j * DI + d] += cm * fabs(ki[d]);
+                            dkm[d] += cm * fabs(q[(int64_t)j * DI + d]);
+                        }
                     }
                 }
             }
@@ -547,12 +616,24 @@ int ora_indexer_kl(int dt, const void *qI, const float *q_scale, const void *kI,
         free(I);
         free(g);
         free(valid);
+        free(R);
+        free(Pn);
+        free(band);
     }
     for (int64_t i = 0; i < rows * DI; ++i) {
-        double acc = 0.0;
-        for (int th = 0; th < nth; ++th)
+        double acc = 0.0, accm = 0.0, acck = 0.0;
+        for (int th = 0; th < nth; ++th) {
             acc += dk_part[(size_t)th * rows * DI + i];
+            if (want_mag) {
+                accm += dk_part[((size_t)nth + th) * rows * DI + i];
+                acck += dk_part[((size_t)2 * nth + th) * rows * DI + i];
+            }
+        }
         dk[i] = acc;
+        if (want_mag) {
+            dk_mag[i] = accm;
+            dk_kink[i] = acck;
+        }
     }
     free(dk_part);
     return 0;

@@ -79,6 +79,14 @@ int main() {
     EXPECT(topk_select_noalloc(nullptr, I64, I32, 64, 2048, 131072, I32, F, nullptr), TLSL_ERR_NULL);
     EXPECT(topk_select_noalloc(F, I64, I32, 64, 4097, 131072, I32, F, nullptr), TLSL_ERR_UNSUPPORTED);
 
+    // ---- indexer_loss_grad
+    EXPECT(indexer_loss_grad(P, P, F, I32, F, 1, 100, 64, 128, 2048, TLSL_BF16, F, F, F, F, nullptr), TLSL_OK);
+    EXPECT(indexer_loss_grad(P, P, F, I32, nullptr, 1, 100, 64, 128, 2048, TLSL_BF16, F, F, F, F, nullptr), TLSL_ERR_NULL);
+    EXPECT(indexer_loss_grad(P, P, F, I32, F, 1, 100, 64, 128, 2048, TLSL_FP8_E4M3, F, F, F, F, nullptr), TLSL_ERR_UNSUPPORTED);
+    EXPECT(indexer_loss_grad(P, P, F, I32, F, 1, 100, 64, 64, 2048, TLSL_BF16, F, F, F, F, nullptr), TLSL_ERR_UNSUPPORTED);
+    EXPECT(indexer_loss_grad(P, P, F, I32, F, 1, 0, 64, 128, 2048, TLSL_BF16, F, F, F, F, nullptr), TLSL_ERR_SHAPE);
+    EXPECT(indexer_loss_grad(P, odd, F, I32, F, 1, 100, 64, 128, 2048, TLSL_BF16, F, F, F, F, nullptr), TLSL_ERR_ALIGN);
+
     // ---- attention
     const float sc = 0.05f;
     EXPECT(sparse_attn_prefill(P, P, I32, 1, 100, 128, 576, 512, 2048, sc, TLSL_BF16, P, F, nullptr, &ws, nullptr), TLSL_OK);
@@ -100,10 +108,10 @@ int main() {
     if (strlen(tlsl_version()) == 0) ++g_fail;
 
     // accepted calls: index_prefill, index_decode, topk_select, topk_select_noalloc (2),
-    // sparse_attn_prefill, dense_attn_prefill, sparse_attn_decode (the last one's
-    // stand-in fails on purpose)
-    if (g_launches != 8) {
-        fprintf(stderr, "expected 8 launches, saw %d\n", g_launches);
+    // indexer_loss_grad, sparse_attn_prefill, dense_attn_prefill, sparse_attn_decode
+    // (the last one's stand-in fails on purpose)
+    if (g_launches != 9) {
+        fprintf(stderr, "expected 9 launches, saw %d\n", g_launches);
         ++g_fail;
     }
     if (g_fail) return 1;

@@ -35,6 +35,11 @@ hipError_t launch_topk_select(const float*, const int64_t*, const int32_t*, int,
     ++g_launches;
     return hipSuccess;
 }
+hipError_t launch_indexer_kl(const void*, const void*, const float*, const int32_t*, const float*, int, int, int,
+                             int, float*, float*, float*, float*, hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
 hipError_t launch_sparse_attn_prefill(const AttnShape&, const void*, const void*, const int32_t*, int, int, int,
                                       float, void*, float*, hipStream_t) {
     ++g_launches;

@@ -236,3 +236,56 @@ def test_quantised_inputs_use_the_decoded_values():
         ref = oracle.indexer_kl(F32, qs.float().numpy(), None, ks.float().numpy(), None, w, S, p)
         for a, b in zip(got, ref):
             np.testing.assert_array_equal(a, b)
+
+
+def test_magnitude_sums_bound_the_results():
+    """The optional magnitude sums (used to scale test tolerances) change no
+    result and bound each result's absolute value; on non-negative inputs with
+    one head and unit weight every mask is open and the dq magnitude is
+    sum_i (R_i + P_i) |k_i| exactly."""
+    q, kk, w, S, p = _random_problem(8)
+    base = oracle.indexer_kl(F32, q, None, kk, None, w, S, p)
+    res = oracle.indexer_kl(F32, q, None, kk, None, w, S, p, want_mags=True)
+    for a, b in zip(base, res[:4]):
+        np.testing.assert_array_equal(a, b)
+    for val, mag in zip(res[:4], res[4:8]):
+        assert (np.abs(val) <= mag * (1 + 1e-12) + 1e-300).all()
+    rng = np.random.default_rng(9)
+    n, DI, k = 12, 3, 4
+    q = rng.random((1, n, 1, DI)).astype(np.float32) + 0.1
+    kk = rng.random((1, n, DI)).astype(np.float32) + 0.1
+    w = np.ones((1, n, 1), np.float32)
+    S = np.full((1, n, k), -1, np.int32)
+    for t in range(n):
+        K = min(k, t + 1)
+        S[0, t, :K] = np.sort(rng.choice(t + 1, K, replace=False))
+    p = rng.random((1, n, k)).astype(np.float32) + 0.1
+    _, _, _, _, _, dqm, _, _, dqk, dkk = oracle.indexer_kl(F32, q, None, kk, None, w, S, p, want_mags=True)
+    assert not dqk.any() and not dkk.any()   # positive inputs: every dot product is far from the kink
+    I = q[0, :, 0].astype(np.float64) @ kk[0].astype(np.float64).T
+    t = n - 1
+    sel = S[0, t]
+    R = softmax(I[t, sel])
+    P = p[0, t].astype(np.float64) / p[0, t].astype(np.float64).sum()
+    np.testing.assert_allclose(dqm[0, t, 0], ((R + P)[:, None] * np.abs(kk[0, sel].astype(np.float64))).sum(0),
+                               rtol=1e-12)
+
+
+def test_kink_band_holds_exactly_the_near_zero_terms():
+    """A dot product that is exactly zero lies in the band (its term is
+    reported at full weight there and not counted in dq); one far from zero
+    does not."""
+    q = np.zeros((1, 2, 1, 2), np.float32)
+    q[0, 1, 0] = [1.0, 0.0]
+    kk = np.array([[[1.0, 0.0], [0.0, 2.0]]], np.float32)
+    w = np.full((1, 2, 1), 0.5, np.float32)
+    S = np.array([[[0, -1], [0, 1]]], np.int32)
+    p = np.array([[[1, 0], [1, 1]]], np.float32)
+    res = oracle.indexer_kl(F32, q, None, kk, None, w, S, p, want_mags=True)
+    dq, dqk, dkk = res[1], res[8], res[9]
+    # row 1: I = (0.5, 0), R = (e^.5, 1)/(e^.5 + 1), P = (1/2, 1/2); key 1 is orthogonal to q
+    R1 = 1.0 / (math.exp(0.5) + 1.0)
+    np.testing.assert_allclose(dqk[0, 1, 0], [0.0, (R1 + 0.5) * 0.5 * 2.0], rtol=1e-14)
+    np.testing.assert_allclose(dkk[0, 1], [(R1 + 0.5) * 0.5 * 1.0, 0.0], rtol=1e-14)
+    assert dq[0, 1, 0, 1] == 0.0
+    assert not dkk[0, 0].any()

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     index_decode,
     index_prefill,
     index_prefill_workspace_bytes,
+    indexer_loss_grad,
     load,
     sparse_attn_decode,
     sparse_attn_decode_workspace_bytes,

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libtlsl.so")
 F32, BF16, FP8_E4M3 = 0, 1, 2
 
 EXPORTS = ("index_prefill", "index_decode", "topk_select", "topk_select_noalloc", "sparse_attn_prefill",
-           "dense_attn_prefill", "sparse_attn_decode", "tlsl_last_error", "tlsl_version",
+           "dense_attn_prefill", "sparse_attn_decode", "indexer_loss_grad", "tlsl_last_error", "tlsl_version",
            # measurement aids (include/tlsl_measure.h)
            "tlsl_timer_arm", "tlsl_timer_collect", "tlsl_calib_copy", "tlsl_calib_mfma")
 
@@ -49,9 +49,10 @@ def load():
     lib.sparse_attn_prefill.argtypes = [P, P, P, I, I, I, I, I, I, F, I, P, P, P, SZ, P]
     lib.dense_attn_prefill.argtypes = [P, P, I, I, I, I, I, F, I, P, P, P, SZ, P]
     lib.sparse_attn_decode.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, P, P, SZ, P]
+    lib.indexer_loss_grad.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P]
     for fn in ("index_prefill", "index_decode", "topk_select", "topk_select_noalloc", "sparse_attn_prefill",
                "dense_attn_prefill",
-               "sparse_attn_decode"):
+               "sparse_attn_decode", "indexer_loss_grad"):
         getattr(lib, fn).restype = I
     lib.tlsl_last_error.restype = ctypes.c_char_p
     lib.tlsl_version.restype = ctypes.c_char_p
@@ -253,6 +254,26 @@ def sparse_attn_decode(q, kv_cache, cu_seqlens, S, softmax_scale, Dv, out=None, 
                                 _ptr(workspace), ctypes.byref(size), _stream(stream))
     _check("sparse_attn_decode", rc)
     return out, lse
+
+
+def indexer_loss_grad(qI, kI, wI, S, p, loss=None, dq=None, dk=None, dw=None, stream=None):
+    """Sparse-stage indexer loss (KL over the selected set) and its gradient:
+    returns (loss [B,n], dq [B,n,HI,dI], dk [B,n,dI], dw [B,n,HI]), fp32."""
+    lib = load()
+    for t, nm in ((qI, "qI"), (kI, "kI"), (wI, "wI"), (S, "S"), (p, "p")):
+        _need(t, nm)
+    B, n, HI, DI = qI.shape
+    k = S.shape[-1]
+    dev = qI.device
+    f32 = torch.float32
+    loss = torch.empty((B, n), dtype=f32, device=dev) if loss is None else loss
+    dq = torch.empty((B, n, HI, DI), dtype=f32, device=dev) if dq is None else dq
+    dk = torch.empty((B, n, DI), dtype=f32, device=dev) if dk is None else dk
+    dw = torch.empty((B, n, HI), dtype=f32, device=dev) if dw is None else dw
+    rc = lib.indexer_loss_grad(_ptr(qI), _ptr(kI), _ptr(wI), _ptr(S), _ptr(p), B, n, HI, DI, k, dtype_code(qI),
+                               _ptr(loss), _ptr(dq), _ptr(dk), _ptr(dw), _stream(stream))
+    _check("indexer_loss_grad", rc)
+    return loss, dq, dk, dw
 
 
 # ---- measurement aids (include/tlsl_measure.h) --------------------------------

@@ -171,6 +171,24 @@ int topk_select_noalloc(const float* scores, const int64_t* row_start, const int
                          "topk_select_noalloc");
 }
 
+int indexer_loss_grad(const void* qI, const void* kI, const float* wI, const int32_t* S, const float* p, int B, int n,
+                      int HI, int dI, int k, tlsl_dtype dt, float* loss, float* dq, float* dk, float* dw,
+                      hipStream_t stream) {
+    if (!qI || !kI || !wI || !S || !p || !loss || !dq || !dk || !dw)
+        return fail(TLSL_ERR_NULL, "indexer_loss_grad: NULL pointer argument");
+    if (B <= 0 || n <= 0 || HI <= 0 || dI <= 0 || k <= 0)
+        return fail(TLSL_ERR_SHAPE, "indexer_loss_grad: B, n, HI, dI and k must be positive");
+    if ((int64_t)B * n > (int64_t)1 << 30) return fail(TLSL_ERR_SHAPE, "indexer_loss_grad: B*n too large");
+    if (dt != TLSL_BF16 || dI != 128 || HI > 64 || k > 4096)
+        return fail(TLSL_ERR_UNSUPPORTED, "indexer_loss_grad: (dtype %s, HI=%d, dI=%d, k=%d) not built "
+                    "(bf16, dI 128, HI 1..64, k 1..4096)", dt_name(dt), HI, dI, k);
+    if (!aligned16(qI) || !aligned16(kI) || !aligned16(wI) || !aligned16(S) || !aligned16(p) || !aligned16(loss) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dw))
+        return fail(TLSL_ERR_ALIGN, "indexer_loss_grad: pointers not 16-byte aligned");
+    return launch_result(tlsl::launch_indexer_kl(qI, kI, wI, S, p, B, n, HI, k, loss, dq, dk, dw, stream),
+                         "indexer_loss_grad");
+}
+
 int sparse_attn_prefill(const void* q, const void* kv, const int32_t* S, int B, int n, int H, int Dqk, int Dv, int k,
                         float softmax_scale, tlsl_dtype dt, void* out, float* lse, void* workspace, size_t* ws_bytes,
                         hipStream_t stream) {

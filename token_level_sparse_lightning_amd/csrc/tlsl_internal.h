@@ -68,6 +68,11 @@ hipError_t launch_topk_select(const float* scores, const int64_t* row_start,
                               const int32_t* row_len, int R, int k, int max_len, int32_t* S,
                               float* S_score, void* ws, hipStream_t st);
 
+// ---- indexer training step (sparse-stage loss and gradient) -----------------------
+hipError_t launch_indexer_kl(const void* q, const void* k, const float* w, const int32_t* S, const float* p,
+                             int B, int n, int HI, int topk, float* loss, float* dq, float* dk, float* dw,
+                             hipStream_t st);
+
 // ---- sparse attention ---------------------------------------------------------
 struct AttnShape {
     int dt;  // 0 f32, 1 bf16
