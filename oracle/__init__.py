@@ -58,6 +58,8 @@ def _load():
         lib.ora_sparse_attn_rows.argtypes = [I, P, P, P, P, I, I, I, I, I, ctypes.c_double, P, P]
         lib.ora_indexer_kl.argtypes = [I, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P]
         lib.ora_indexer_kl_mag.argtypes = [I, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.ora_selection_quality.argtypes = [P, P, P, I, P, I, I, P, P]
+        lib.ora_cutoff_margin.argtypes = [P, P, P, I, I, P]
         lib.ora_num_threads.restype = I
         _lib = lib
     return _lib
@@ -256,3 +258,34 @@ def indexer_kl(dt, q, q_scale, k_in, k_scale, w, S, p, want_mags=False):
                                   _ptr(S), _ptr(p), _ptr(loss), _ptr(dq), _ptr(dk), _ptr(dw), *(_ptr(m) for m in mags)),
            "indexer_kl")
     return (loss, dq, dk, dw) + mags
+
+
+def selection_quality(teacher, row_start, row_len, S, m):
+    """Recall of the teacher's top-m (DSA page eq.(9); eq.(14) is m = k) and
+    teacher mass coverage (eq.(15), teacher normalised over the row) of the
+    selections S [R,k] (row-relative).  Returns (recall [R], mass [R])."""
+    lib = _load()
+    teacher = _c(teacher, np.float32)
+    row_start = _c(row_start, np.int64)
+    row_len = _c(row_len, np.int32)
+    S = _c(S, np.int32)
+    R, k = S.shape
+    recall = np.empty(R, np.float64)
+    mass = np.empty(R, np.float64)
+    _check(lib.ora_selection_quality(_ptr(teacher), _ptr(row_start), _ptr(row_len), R, _ptr(S), k, int(m),
+                                     _ptr(recall), _ptr(mass)), "selection_quality")
+    return recall, mass
+
+
+def cutoff_margin(scores, row_start, row_len, k):
+    """Cutoff margin s_(K) - s_(K+1) of each score row (eq.(18)), +inf when
+    the row has no (K+1)-th score."""
+    lib = _load()
+    scores = _c(scores, np.float32)
+    row_start = _c(row_start, np.int64)
+    row_len = _c(row_len, np.int32)
+    R = len(row_len)
+    margin = np.empty(R, np.float64)
+    _check(lib.ora_cutoff_margin(_ptr(scores), _ptr(row_start), _ptr(row_len), R, int(k), _ptr(margin)),
+           "cutoff_margin")
+    return margin

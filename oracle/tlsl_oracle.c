@@ -639,6 +639,81 @@ int ora_indexer_kl_mag(int dt, const void *qI, const float *q_scale, const void 
     return 0;
 }
 
+/* ---- selection-quality diagnostics (DSA page, sections 1.2 and 3.1) -----
+ *
+ * For row r, teacher masses a[0..L) (L = row_len[r], at row_start[r]) and a
+ * selection S_r (k slots; entries outside [0, L) are not selected, a repeated
+ * entry counts once):
+ *   G       = TopK(a, min(m, L)) by the rule of eq.(2) (ties to the lower
+ *             position)
+ *   recall  = |G n S_r| / |G|                      eq.(9); eq.(14) is m = k
+ *   mass    = sum_{s in S_r} a_s / sum_{s < L} a_s  eq.(15) with the teacher
+ *             normalised over the row
+ * recall is NaN when G is empty, mass when the row's total is not positive. */
+int ora_selection_quality(const float *teacher, const int64_t *row_start, const int32_t *row_len,
+                          int R, const int32_t *S, int k, int m, double *recall, double *mass)
+{
+    if (!teacher || !row_start || !row_len || !S || !recall || !mass || R < 0 || k <= 0 || m <= 0)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < R; ++r) {
+        const int64_t L = row_len[r] > 0 ? row_len[r] : 0;
+        const float *a = teacher + row_start[r];
+        const int32_t *Sr = S + (int64_t)r * k;
+        char *in_s = calloc((size_t)(L > 0 ? L : 1), 1);
+        for (int i = 0; i < k; ++i)
+            if (Sr[i] >= 0 && Sr[i] < L)
+                in_s[Sr[i]] = 1;
+        double total = 0.0, covered = 0.0;
+        for (int64_t s = 0; s < L; ++s) {
+            total += (double)a[s];
+            if (in_s[s])
+                covered += (double)a[s];
+        }
+        mass[r] = total > 0.0 ? covered / total : NAN;
+        int32_t *G = malloc(sizeof(int32_t) * (size_t)m);
+        select_row(a, L, m, G, NULL);
+        int64_t ng = 0, hit = 0;
+        for (int i = 0; i < m; ++i) {
+            if (G[i] < 0)
+                continue;
+            ++ng;
+            hit += in_s[G[i]];
+        }
+        recall[r] = ng > 0 ? (double)hit / (double)ng : NAN;
+        free(G);
+        free(in_s);
+    }
+    return 0;
+}
+
+/* eq.(18): the cutoff margin s_(K) - s_(K+1) of each score row, K = min(k, L),
+ * s_(1) >= s_(2) >= ... the row's scores in descending order; +inf when the
+ * row has no (K+1)-th score (L <= k). */
+int ora_cutoff_margin(const float *scores, const int64_t *row_start, const int32_t *row_len, int R,
+                      int k, double *margin)
+{
+    if (!scores || !row_start || !row_len || !margin || R < 0 || k <= 0)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < R; ++r) {
+        const int64_t L = row_len[r] > 0 ? row_len[r] : 0;
+        if (L <= k) {
+            margin[r] = INFINITY;
+            continue;
+        }
+        ora_cand *c = malloc(sizeof(ora_cand) * (size_t)L);
+        for (int64_t s = 0; s < L; ++s) {
+            c[s].score = scores[row_start[r] + s];
+            c[s].pos = (int32_t)s;
+        }
+        qsort(c, (size_t)L, sizeof(ora_cand), cmp_rank);
+        margin[r] = (double)c[k - 1].score - (double)c[k].score;
+        free(c);
+    }
+    return 0;
+}
+
 int ora_num_threads(void)
 {
     int n = 1;
