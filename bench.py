@@ -14,6 +14,8 @@ other rows of the path, each on its own workload (``extra``):
   attn_prefill_32768   sparse_attn_prefill over that selection
   attn_dense_2048      dense_attn_prefill (short prefill: n <= k, every query
                        over all of its history), n=2048, H=128
+  dispatch_2048        dsa_prefill at n = k = 2048 (dense path: every row keeps
+                       all history) against index_prefill + sparse_attn_prefill
   decode               one decode step of 64 ragged sequences
                        (L ~ U[16384,131072]): index_decode + topk_select +
                        sparse_attn_decode, tokens/s
@@ -235,6 +237,39 @@ def bench_train(seed, steps, warmup):
                 frac=ach / PEAK_BF16_TFLOPS, **tm.as_dict())
 
 
+def bench_dispatch(seed, steps, warmup):
+    """dsa_prefill at n = k = 2048 (every row keeps all history, so it takes
+    the dense path) against the two-call sparse path on the same inputs
+    (fp8 indexer H^I=64, d^I=128; bf16 attention H=128, 576/512)."""
+    n, k, H, Dqk, Dv = 2048, 2048, 128, 576, 512
+    ix = synth.indexer_prefill(1, n, 64, 128, synth.DT_FP8, seed, planted=True, device=DEV)
+    q, kv = synth.attn_prefill(1, n, H, Dqk, synth.DT_BF16, seed, device=DEV)
+    scale = 1.0 / math.sqrt(Dqk)
+    out = torch.empty((1, n, H, Dv), dtype=torch.bfloat16, device=DEV)
+    S = torch.empty((1, n, k), dtype=torch.int32, device=DEV)
+    ws = torch.empty(tl.index_prefill_workspace_bytes(ix.q, ix.k, ix.w, k, ix.q_scale, ix.k_scale), dtype=torch.uint8,
+                     device=DEV)
+    dws = torch.empty(256, dtype=torch.uint8, device=DEV)
+
+    def dispatched():
+        tl.dsa_prefill(ix.q, ix.k, ix.w, q, kv, k, scale, Dv, q_scale=ix.q_scale, k_scale=ix.k_scale, out=out,
+                       workspace=dws)
+
+    def two_calls():
+        tl.index_prefill(ix.q, ix.k, ix.w, k, q_scale=ix.q_scale, k_scale=ix.k_scale, S=S, workspace=ws)
+        tl.sparse_attn_prefill(q, kv, S, scale, Dv, out=out)
+
+    td = time_calls(dispatched, steps, warmup)
+    ts = time_calls(two_calls, steps, warmup)
+    log(f"dispatch n={n} k={k}: dsa_prefill (dense path) {td.ev_med:.3f} ms, index_prefill + sparse_attn_prefill "
+        f"{ts.ev_med:.3f} ms")
+    del ix, q, kv, out, S, ws
+    return dict(workload=f"prefill path chosen by length: n={n}, k={k} (every row keeps all history), fp8 indexer "
+                         f"H^I=64 d^I=128, bf16 attention H={H} Dqk={Dqk} Dv={Dv}",
+                dsa_prefill_dense_path=td.as_dict(), index_prefill_plus_sparse_attn=ts.as_dict(),
+                speedup=ts.ev_med / td.ev_med)
+
+
 def bench_tiny(steps, warmup):
     """The tiny fp32 configuration (dyadic indexer inputs, exact scores):
     index_prefill and sparse_attn_prefill timed separately; report only."""
@@ -275,6 +310,28 @@ def decode_stage_bytes(lengths, HI, DI, H, Dqk, Dv, k):
         # gathered entries, queries, S, outputs
         "sparse_attn_kernel": float((K * Dqk * 2).sum() + B * H * Dqk * 2 + B * k * 4 + B * H * Dv * 2),
     }
+
+
+def _margin_ws_bytes(R, k, max_len):
+    """Workspace size of cutoff_margin (size query through the C ABI)."""
+    import ctypes
+    lib = tl.load()
+    size = ctypes.c_size_t(0)
+    d = ctypes.c_void_p(16)
+    rc = lib.cutoff_margin(d, d, d, int(R), int(k), int(max_len), d, None, ctypes.byref(size), None)
+    assert rc == 0, lib.tlsl_last_error()
+    return size.value
+
+
+def _quality_ws_bytes(R, k, m, max_len):
+    """Workspace size of selection_quality (size query through the C ABI)."""
+    import ctypes
+    lib = tl.load()
+    size = ctypes.c_size_t(0)
+    d = ctypes.c_void_p(16)
+    rc = lib.selection_quality(d, d, d, int(R), d, int(k), int(m), int(max_len), d, d, None, ctypes.byref(size), None)
+    assert rc == 0, lib.tlsl_last_error()
+    return size.value
 
 
 def bench_decode(seed, steps, warmup):
@@ -331,6 +388,28 @@ def bench_decode(seed, steps, warmup):
         "; ".join(f"{n_}: {v['event_ms_median']:.3f} ms (" +
                   ", ".join(f"{kn} {kv['kernel_ms_avg']:.3f} ms" + (f" {kv['gbs']:.0f} GB/s" if 'gbs' in kv else "")
                             for kn, kv in v["kernels"].items()) + ")" for n_, v in stages.items()))
+    # selection-quality diagnostics on the step's rows: the cutoff margin of
+    # the indexer scores and recall / mass of a synthetic teacher (mass 1 on
+    # each sequence's planted keys, a small uniform floor elsewhere)
+    teacher = torch.full_like(scores, 1e-4)
+    for b, pos in di.planted.items():
+        teacher[int(cu[b]) + torch.as_tensor(pos, device=DEV)] = 1.0
+    mg = torch.empty(B, dtype=torch.float32, device=DEV)
+    rec = torch.empty(B, dtype=torch.float32, device=DEV)
+    mass = torch.empty(B, dtype=torch.float32, device=DEV)
+    mws = torch.empty(_margin_ws_bytes(B, k, max_len), dtype=torch.uint8, device=DEV)
+    qws = torch.empty(_quality_ws_bytes(B, k, 32, max_len), dtype=torch.uint8, device=DEV)
+
+    def f_diag():
+        tl.cutoff_margin(scores, row_start, row_len, k, max_len, margin=mg, workspace=mws)
+        tl.selection_quality(teacher, row_start, row_len, S, 32, max_len, recall=rec, mass=mass, workspace=qws)
+
+    tdg = time_calls(f_diag, max(5, steps // 2), 2)
+    diag = dict(event_ms_median=tdg.ev_med, teacher_bytes=float(lengths.sum() * 4),
+                margin_median=float(mg.median()), recall_top32_mean=float(rec.mean()), mass_mean=float(mass.mean()))
+    log(f"decode diagnostics: cutoff_margin + selection_quality {tdg.ev_med:.3f} ms; margin median "
+        f"{diag['margin_median']:.3g}, recall of the planted keys {diag['recall_top32_mean']:.3f}, "
+        f"mass {diag['mass_mean']:.3f}")
     Sh = S.cpu().numpy()
     hit = tot = 0
     for b, pos in di.planted.items():
@@ -343,6 +422,7 @@ def bench_decode(seed, steps, warmup):
                          f"fp8 indexer H^I={HI} d^I={DI}, top-{k}, bf16 attention H={H} Dqk={Dqk} Dv={Dv}",
                 tokens_per_s=B / (tm.wall * 1e-3), bytes_per_step=nbytes, achieved_gbs=gbs,
                 peak_gbs=PEAK_HBM_GBS, frac=gbs / PEAK_HBM_GBS, stages=stages, planted_recall=planted_hit,
+                diagnostics=diag,
                 **tm.as_dict())
 
 
@@ -429,7 +509,7 @@ def recorded_traffic(kernel, workload):
 
 
 EXTRAS = ("attn_prefill_131072", "prefill_bf16_8192", "prefill_fp8_32768", "attn_prefill_32768",
-          "attn_dense_2048", "decode", "train_8192", "tiny_f32_512")
+          "attn_dense_2048", "dispatch_2048", "decode", "train_8192", "tiny_f32_512")
 
 
 def main():
@@ -481,6 +561,9 @@ def main():
         torch.cuda.empty_cache()
     if "attn_dense_2048" in want:
         extra["attn_dense_2048"] = bench_attn_dense(2048, 6, max(5, args.steps // 2), 2)
+        torch.cuda.empty_cache()
+    if "dispatch_2048" in want:
+        extra["dispatch_2048"] = bench_dispatch(7, max(5, args.steps // 2), 2)
         torch.cuda.empty_cache()
     if "decode" in want:
         extra["decode"] = bench_decode(4, args.steps, args.warmup)

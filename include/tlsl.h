@@ -195,6 +195,43 @@ int indexer_loss_grad(const void* qI, const void* kI, const float* wI, const int
                       float* loss, float* dq, float* dk, float* dw, hipStream_t stream);
 
 /*
+ * selection_quality -- how much of a teacher distribution each row's
+ * selection covers (DSA page, section 1.2 eq.(9); section 3.1 eq.(14), (15)).
+ * Row r of `teacher` holds masses a_0..a_{L-1} (L = row_len[r], at
+ * row_start[r]; >= 0, not necessarily normalised), e.g. the main attention's
+ * probabilities summed over heads.  With G = TopK(a, min(m, L)) by the rule of
+ * eq.(2) (ties to the lower position):
+ *     recall[r] = |G n S_r| / |G|          eq.(9); eq.(14) is m = k
+ *     mass[r]   = sum_{s in S_r} a_s / sum_{s < L} a_s        eq.(15)
+ * NaN where |G| = 0 or the row's total is not positive.
+ *
+ *   teacher, row_start, row_len, R, max_len: as topk_select's scores rows
+ *   S      [R,k] int32 row-relative selections in the library's layout
+ *          (ascending positions, then -1); positions >= L are ignored
+ *   m      1..4096;  recall, mass [R] fp32 out
+ *   workspace: query protocol (the teacher's top-m and topk_select's).
+ * Sums run in fp64 (mass is the fp64 ratio rounded once to fp32).
+ */
+int selection_quality(const float* teacher, const int64_t* row_start, const int32_t* row_len,
+                      int R, const int32_t* S, int k, int m, int max_len, float* recall,
+                      float* mass, void* workspace, size_t* ws_bytes, hipStream_t stream);
+
+/*
+ * cutoff_margin -- the cutoff margin of each score row (DSA page, section 3.1
+ * eq.(18)): margin[r] = s_(K) - s_(K+1), K = min(k, L), s_(1) >= s_(2) >= ...
+ * the row's scores in descending order; +inf when the row has no (K+1)-th
+ * score (L <= k).  A small margin means a small perturbation of the scores
+ * (fp8 quantisation, rounding) can swap the selection's boundary keys.
+ *
+ *   scores, row_start, row_len, R, max_len: as topk_select
+ *   margin [R] fp32 out (the fp32 difference of the two scores, rounded once)
+ * Supported: 1 <= k <= 4095.  Workspace: query protocol.
+ */
+int cutoff_margin(const float* scores, const int64_t* row_start, const int32_t* row_len, int R,
+                  int k, int max_len, float* margin, void* workspace, size_t* ws_bytes,
+                  hipStream_t stream);
+
+/*
  * sparse_attn_prefill -- attention of every query over its selected shared
  * latent entries (DSA page, section 1.1 eq.(3); the Sparse MLA paragraph after
  * eq.(1) gathers the latent KV named by S[t,:]).  For query (b,t), head h and
@@ -236,6 +273,34 @@ int sparse_attn_prefill(const void* q, const void* kv, const int32_t* S, int B, 
 int dense_attn_prefill(const void* q, const void* kv, int B, int n, int H, int Dqk, int Dv,
                        float softmax_scale, tlsl_dtype dt, void* out, float* lse,
                        void* workspace, size_t* ws_bytes, hipStream_t stream);
+
+/*
+ * dsa_prefill -- the whole prefill path with the choice of kernels made by
+ * length: the DSA page, section 2 (the short-prefill paragraph), notes that
+ * for short sequences the top-k, index materialisation and gather cost more
+ * than they save and that serving should pick the path by length and batch.
+ * When n <= k, TopK(min(k, t+1)) (section 1.1 eq.(2)) keeps every position of
+ * every row, so the indexer is skipped and the causal attention over all
+ * history runs directly (dense_attn_prefill's path); otherwise index_prefill
+ * and sparse_attn_prefill run back to back.  Both paths give the result of
+ * the two-call sequence bit for bit (the same attention kernel and slot
+ * order).
+ *
+ *   indexer inputs as index_prefill (qI, q_scale, kI, k_scale, wI, HI, dI,
+ *   idx_dt); attention inputs as sparse_attn_prefill (q, kv, H, Dqk, Dv,
+ *   softmax_scale, attn_dt); B, n, k.
+ *   S    [B,n,k] int32 out, optional: the selection (on the dense path
+ *        0..t then -1); when NULL the sparse path keeps it in the workspace
+ *   out  [B,n,H,Dv], lse [B,n,H] (optional)
+ *   workspace: query protocol; on the sparse path index_prefill's workspace
+ *   (plus S when S is NULL), on the dense path 256 bytes.
+ * Supported shapes: those of index_prefill and sparse_attn_prefill.
+ */
+int dsa_prefill(const void* qI, const float* q_scale, const void* kI, const float* k_scale,
+                const float* wI, int HI, int dI, tlsl_dtype idx_dt, const void* q, const void* kv,
+                int H, int Dqk, int Dv, float softmax_scale, tlsl_dtype attn_dt, int B, int n,
+                int k, int32_t* S, void* out, float* lse, void* workspace, size_t* ws_bytes,
+                hipStream_t stream);
 
 /*
  * sparse_attn_decode -- as sparse_attn_prefill for the newest token of each

@@ -12,6 +12,7 @@
 
 extern int g_launches;
 static int g_fail = 0;
+static float sc0() { return 0.05f; }
 
 #define EXPECT(call, code)                                                                       \
     do {                                                                                         \
@@ -87,6 +88,33 @@ int main() {
     EXPECT(indexer_loss_grad(P, P, F, I32, F, 1, 0, 64, 128, 2048, TLSL_BF16, F, F, F, F, nullptr), TLSL_ERR_SHAPE);
     EXPECT(indexer_loss_grad(P, odd, F, I32, F, 1, 100, 64, 128, 2048, TLSL_BF16, F, F, F, F, nullptr), TLSL_ERR_ALIGN);
 
+    // ---- dsa_prefill: dense path (n <= k: fill S + attention), sparse path (prefill + attention)
+    EXPECT(dsa_prefill(P, F, P, F, F, 64, 128, TLSL_FP8_E4M3, P, P, 128, 576, 512, sc0(), TLSL_BF16, 1, 2048, 2048, I32,
+                       P, F, nullptr, &need, nullptr), TLSL_OK);
+    ws = need;
+    EXPECT(dsa_prefill(P, F, P, F, F, 64, 128, TLSL_FP8_E4M3, P, P, 128, 576, 512, sc0(), TLSL_BF16, 1, 2048, 2048, I32,
+                       P, F, P, &ws, nullptr), TLSL_OK);
+    EXPECT(dsa_prefill(P, F, P, F, F, 64, 128, TLSL_FP8_E4M3, P, P, 128, 576, 512, sc0(), TLSL_BF16, 1, 4096, 2048,
+                       nullptr, P, F, nullptr, &need, nullptr), TLSL_OK);
+    ws = need;
+    EXPECT(dsa_prefill(P, F, P, F, F, 64, 128, TLSL_FP8_E4M3, P, P, 128, 576, 512, sc0(), TLSL_BF16, 1, 4096, 2048,
+                       nullptr, P, F, P, &ws, nullptr), TLSL_OK);
+    EXPECT(dsa_prefill(P, F, P, F, F, 64, 128, TLSL_FP8_E4M3, P, P, 127, 576, 500, sc0(), TLSL_BF16, 1, 4096, 2048,
+                       nullptr, P, F, P, &ws, nullptr), TLSL_ERR_UNSUPPORTED);
+    EXPECT(dsa_prefill(P, F, P, F, F, 64, 128, TLSL_FP8_E4M3, nullptr, P, 128, 576, 512, sc0(), TLSL_BF16, 1, 4096,
+                       2048, nullptr, P, F, P, &ws, nullptr), TLSL_ERR_NULL);
+
+    // ---- selection_quality / cutoff_margin
+    EXPECT(selection_quality(F, I64, I32, 64, I32, 2048, 64, 131072, F, F, nullptr, &need, nullptr), TLSL_OK);
+    ws = need;
+    EXPECT(selection_quality(F, I64, I32, 64, I32, 2048, 64, 131072, F, F, P, &ws, nullptr), TLSL_OK);
+    EXPECT(selection_quality(F, I64, I32, 64, nullptr, 2048, 64, 131072, F, F, P, &ws, nullptr), TLSL_ERR_NULL);
+    EXPECT(selection_quality(F, I64, I32, 64, I32, 2048, 5000, 131072, F, F, P, &ws, nullptr), TLSL_ERR_UNSUPPORTED);
+    EXPECT(cutoff_margin(F, I64, I32, 64, 2048, 131072, F, nullptr, &need, nullptr), TLSL_OK);
+    ws = need;
+    EXPECT(cutoff_margin(F, I64, I32, 64, 2048, 131072, F, P, &ws, nullptr), TLSL_OK);
+    EXPECT(cutoff_margin(F, I64, I32, 64, 4096, 131072, F, P, &ws, nullptr), TLSL_ERR_UNSUPPORTED);
+
     // ---- attention
     const float sc = 0.05f;
     EXPECT(sparse_attn_prefill(P, P, I32, 1, 100, 128, 576, 512, 2048, sc, TLSL_BF16, P, F, nullptr, &ws, nullptr), TLSL_OK);
@@ -108,10 +136,11 @@ int main() {
     if (strlen(tlsl_version()) == 0) ++g_fail;
 
     // accepted calls: index_prefill, index_decode, topk_select, topk_select_noalloc (2),
-    // indexer_loss_grad, sparse_attn_prefill, dense_attn_prefill, sparse_attn_decode
-    // (the last one's stand-in fails on purpose)
-    if (g_launches != 9) {
-        fprintf(stderr, "expected 9 launches, saw %d\n", g_launches);
+    // indexer_loss_grad, dsa_prefill dense (fill + attention) and sparse (index +
+    // attention), selection_quality, cutoff_margin, sparse_attn_prefill, dense_attn_prefill, sparse_attn_decode (the
+    // last one's stand-in fails on purpose)
+    if (g_launches != 15) {
+        fprintf(stderr, "expected 15 launches, saw %d\n", g_launches);
         ++g_fail;
     }
     if (g_fail) return 1;

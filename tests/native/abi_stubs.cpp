@@ -40,8 +40,22 @@ hipError_t launch_indexer_kl(const void*, const void*, const float*, const int32
     ++g_launches;
     return hipSuccess;
 }
+hipError_t launch_selection_quality(const float*, const int64_t*, const int32_t*, int, const int32_t*, int, int, int,
+                                    float*, float*, void*, hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
+hipError_t launch_cutoff_margin(const float*, const int64_t*, const int32_t*, int, int, int, float*, void*,
+                                hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
 hipError_t launch_sparse_attn_prefill(const AttnShape&, const void*, const void*, const int32_t*, int, int, int,
                                       float, void*, float*, hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
+hipError_t launch_fill_all_history(int32_t*, int, int, int, hipStream_t) {
     ++g_launches;
     return hipSuccess;
 }

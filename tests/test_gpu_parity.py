@@ -477,3 +477,45 @@ def test_max_len_below_the_lengths_is_still_exact():
     S_o, Ss_o = oracle.topk_rows(sc_ok.cpu().numpy(), host(inp.cu_seqlens)[:-1], lengths, 2048)
     np.testing.assert_array_equal(S_small.cpu().numpy(), S_o)
     np.testing.assert_array_equal(Ss_small.cpu().numpy(), Ss_o)
+
+
+# ---------------------------------------------------------------------------
+# dsa_prefill: the path chosen by length
+# ---------------------------------------------------------------------------
+def test_dsa_prefill_dense_path_when_n_le_k():
+    """n <= k: every row keeps all history; dsa_prefill skips the indexer and
+    must equal both dense_attn_prefill and index_prefill + sparse_attn_prefill
+    bit for bit, with S = 0..t then -1."""
+    B, n, k, H = 2, 300, 512, 32
+    ix = synth.indexer_prefill(B, n, 16, 64, BF16, seed=51, device=DEV)
+    q, kv = synth.attn_prefill(B, n, H, 576, BF16, seed=52)
+    qd, kvd = to_dev(q), to_dev(kv)
+    announce("dsa_prefill dense path")
+    out, lse, S = tl.dsa_prefill(ix.q, ix.k, ix.w, qd, kvd, k, 0.05, 512, want_S=True, want_lse=True)
+    o_d, l_d = tl.dense_attn_prefill(qd, kvd, 0.05, 512, want_lse=True)
+    S2, _ = tl.index_prefill(ix.q, ix.k, ix.w, k)
+    o_s, l_s = tl.sparse_attn_prefill(qd, kvd, S2, 0.05, 512, want_lse=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(S.cpu().numpy(), np.concatenate(
+        [_all_history(B, n), np.full((B, n, k - n), -1, np.int32)], axis=2))
+    assert torch.equal(S, S2)
+    assert torch.equal(out, o_d) and torch.equal(lse, l_d)
+    assert torch.equal(out, o_s) and torch.equal(lse, l_s)
+
+
+@pytest.mark.parametrize("keep_S", [True, False])
+def test_dsa_prefill_sparse_path_when_n_gt_k(keep_S):
+    """n > k: indexer, top-k and gather, equal to the two calls bit for bit;
+    without an S argument the selection lives in the workspace."""
+    n, k, H = 1500, 256, 128
+    ix = synth.indexer_prefill(1, n, 64, 128, FP8, seed=53, planted=True, device=DEV)
+    q, kv = synth.attn_prefill(1, n, H, 576, BF16, seed=54, device=DEV)
+    announce(f"dsa_prefill sparse path keep_S={keep_S}")
+    out, lse, S = tl.dsa_prefill(ix.q, ix.k, ix.w, q, kv, k, 1 / 24.0, 512, q_scale=ix.q_scale, k_scale=ix.k_scale,
+                                 want_S=keep_S, want_lse=True)
+    S2, _ = tl.index_prefill(ix.q, ix.k, ix.w, k, q_scale=ix.q_scale, k_scale=ix.k_scale)
+    o2, l2 = tl.sparse_attn_prefill(q, kv, S2, 1 / 24.0, 512, want_lse=True)
+    torch.cuda.synchronize()
+    if keep_S:
+        assert torch.equal(S, S2)
+    assert torch.equal(out, o2) and torch.equal(lse, l2)

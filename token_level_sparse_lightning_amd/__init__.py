@@ -10,12 +10,15 @@ from .binding import (  # noqa: F401
     TlslError,
     calib_copy,
     calib_mfma,
+    cutoff_margin,
     dense_attn_prefill,
+    dsa_prefill,
     index_decode,
     index_prefill,
     index_prefill_workspace_bytes,
     indexer_loss_grad,
     load,
+    selection_quality,
     sparse_attn_decode,
     sparse_attn_decode_workspace_bytes,
     sparse_attn_prefill,

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libtlsl.so")
 F32, BF16, FP8_E4M3 = 0, 1, 2
 
 EXPORTS = ("index_prefill", "index_decode", "topk_select", "topk_select_noalloc", "sparse_attn_prefill",
-           "dense_attn_prefill", "sparse_attn_decode", "indexer_loss_grad", "tlsl_last_error", "tlsl_version",
+           "dense_attn_prefill", "dsa_prefill", "sparse_attn_decode", "indexer_loss_grad", "selection_quality", "cutoff_margin",
+           "tlsl_last_error", "tlsl_version",
            # measurement aids (include/tlsl_measure.h)
            "tlsl_timer_arm", "tlsl_timer_collect", "tlsl_calib_copy", "tlsl_calib_mfma")
 
@@ -50,9 +51,12 @@ def load():
     lib.dense_attn_prefill.argtypes = [P, P, I, I, I, I, I, F, I, P, P, P, SZ, P]
     lib.sparse_attn_decode.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, P, P, SZ, P]
     lib.indexer_loss_grad.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P]
+    lib.dsa_prefill.argtypes = [P, P, P, P, P, I, I, I, P, P, I, I, I, F, I, I, I, I, P, P, P, P, SZ, P]
+    lib.selection_quality.argtypes = [P, P, P, I, P, I, I, I, P, P, P, SZ, P]
+    lib.cutoff_margin.argtypes = [P, P, P, I, I, I, P, P, SZ, P]
     for fn in ("index_prefill", "index_decode", "topk_select", "topk_select_noalloc", "sparse_attn_prefill",
                "dense_attn_prefill",
-               "sparse_attn_decode", "indexer_loss_grad"):
+               "sparse_attn_decode", "indexer_loss_grad", "dsa_prefill", "selection_quality", "cutoff_margin"):
         getattr(lib, fn).restype = I
     lib.tlsl_last_error.restype = ctypes.c_char_p
     lib.tlsl_version.restype = ctypes.c_char_p
@@ -222,6 +226,68 @@ def dense_attn_prefill(q, kv, softmax_scale, Dv, out=None, lse=None, want_lse=Fa
                                 dtype_code(q), _ptr(out), _ptr(lse), None, None, _stream(stream))
     _check("dense_attn_prefill", rc)
     return out, lse
+
+
+def dsa_prefill(qI, kI, wI, q, kv, k, softmax_scale, Dv, q_scale=None, k_scale=None, S=None, want_S=False,
+                out=None, lse=None, want_lse=False, workspace=None, stream=None):
+    """The whole prefill path, dense when n <= k (every row keeps all of its
+    history), indexer + top-k + sparse attention otherwise:
+    returns (out [B,n,H,Dv], lse or None, S or None)."""
+    lib = load()
+    for t, nm in ((qI, "qI"), (kI, "kI"), (wI, "wI"), (q, "q"), (kv, "kv")):
+        _need(t, nm)
+    B, n, HI, DI = qI.shape
+    H, Dqk = q.shape[2], q.shape[3]
+    dev = q.device
+    if S is None and want_S:
+        S = torch.empty((B, n, k), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((B, n, H, Dv), dtype=q.dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, n, H), dtype=torch.float32, device=dev)
+    args = [_ptr(qI), _ptr(q_scale), _ptr(kI), _ptr(k_scale), _ptr(wI), HI, DI, dtype_code(qI), _ptr(q), _ptr(kv), H,
+            Dqk, Dv, float(softmax_scale), dtype_code(q), B, n, k, _ptr(S), _ptr(out), _ptr(lse)]
+    if workspace is None:
+        size = ctypes.c_size_t(0)
+        _check("dsa_prefill", lib.dsa_prefill(*args, None, ctypes.byref(size), None))
+        workspace = torch.empty(size.value, dtype=torch.uint8, device=dev)
+    size = ctypes.c_size_t(workspace.numel())
+    _check("dsa_prefill", lib.dsa_prefill(*args, _ptr(workspace), ctypes.byref(size), _stream(stream)))
+    return out, lse, S
+
+
+def _with_workspace(fn, args, device, workspace, stream):
+    """Call a workspace-protocol entry point: size query, then the call."""
+    lib = load()
+    if workspace is None:
+        size = ctypes.c_size_t(0)
+        _check(fn, getattr(lib, fn)(*args, None, ctypes.byref(size), None))
+        workspace = torch.empty(max(size.value, 1), dtype=torch.uint8, device=device)
+    size = ctypes.c_size_t(workspace.numel())
+    _check(fn, getattr(lib, fn)(*args, _ptr(workspace), ctypes.byref(size), _stream(stream)))
+
+
+def selection_quality(teacher, row_start, row_len, S, m, max_len, recall=None, mass=None, workspace=None,
+                      stream=None):
+    """Recall of the teacher's top-m and teacher mass coverage of the
+    selections S [R,k]: returns (recall [R], mass [R]) fp32."""
+    R, k = S.shape
+    dev = S.device
+    recall = torch.empty(R, dtype=torch.float32, device=dev) if recall is None else recall
+    mass = torch.empty(R, dtype=torch.float32, device=dev) if mass is None else mass
+    _with_workspace("selection_quality", [_ptr(teacher), _ptr(row_start), _ptr(row_len), R, _ptr(S), k, int(m),
+                                          int(max_len), _ptr(recall), _ptr(mass)], dev, workspace, stream)
+    return recall, mass
+
+
+def cutoff_margin(scores, row_start, row_len, k, max_len, margin=None, workspace=None, stream=None):
+    """Cutoff margin s_(K) - s_(K+1) of each score row: returns margin [R] fp32."""
+    R = row_len.shape[0]
+    dev = scores.device
+    margin = torch.empty(R, dtype=torch.float32, device=dev) if margin is None else margin
+    _with_workspace("cutoff_margin", [_ptr(scores), _ptr(row_start), _ptr(row_len), R, int(k), int(max_len),
+                                      _ptr(margin)], dev, workspace, stream)
+    return margin
 
 
 def sparse_attn_decode_workspace_bytes(q, kv_cache, S, Dv) -> int:

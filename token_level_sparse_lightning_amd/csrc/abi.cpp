@@ -189,6 +189,35 @@ int indexer_loss_grad(const void* qI, const void* kI, const float* wI, const int
                          "indexer_loss_grad");
 }
 
+int selection_quality(const float* teacher, const int64_t* row_start, const int32_t* row_len, int R, const int32_t* S,
+                      int k, int m, int max_len, float* recall, float* mass, void* workspace, size_t* ws_bytes,
+                      hipStream_t stream) {
+    if (!S || !recall || !mass) return fail(TLSL_ERR_NULL, "selection_quality: NULL pointer argument");
+    if (k <= 0) return fail(TLSL_ERR_SHAPE, "selection_quality: k=%d must be positive", k);
+    int rc = check_topk(teacher, row_start, row_len, R, m, max_len, S, nullptr, "selection_quality");
+    if (rc) return rc;
+    if (!aligned16(recall) || !aligned16(mass)) return fail(TLSL_ERR_ALIGN, "selection_quality: pointers not 16-byte aligned");
+    rc = workspace_protocol(workspace, ws_bytes, tlsl::selection_quality_ws_bytes(R, m, max_len));
+    if (rc) return rc > 0 ? ok() : rc;
+    return launch_result(tlsl::launch_selection_quality(teacher, row_start, row_len, R, S, k, m, max_len, recall, mass,
+                                                        workspace, stream),
+                         "selection_quality");
+}
+
+int cutoff_margin(const float* scores, const int64_t* row_start, const int32_t* row_len, int R, int k, int max_len,
+                  float* margin, void* workspace, size_t* ws_bytes, hipStream_t stream) {
+    if (!margin) return fail(TLSL_ERR_NULL, "cutoff_margin: margin is NULL");
+    if (k >= 4096) return fail(TLSL_ERR_UNSUPPORTED, "cutoff_margin: k=%d above the supported 4095", k);
+    int32_t dummy_s alignas(16) = 0;
+    int rc = check_topk(scores, row_start, row_len, R, k, max_len, &dummy_s, nullptr, "cutoff_margin");
+    if (rc) return rc;
+    if (!aligned16(margin)) return fail(TLSL_ERR_ALIGN, "cutoff_margin: margin not 16-byte aligned");
+    rc = workspace_protocol(workspace, ws_bytes, tlsl::cutoff_margin_ws_bytes(R, k, max_len));
+    if (rc) return rc > 0 ? ok() : rc;
+    return launch_result(tlsl::launch_cutoff_margin(scores, row_start, row_len, R, k, max_len, margin, workspace, stream),
+                         "cutoff_margin");
+}
+
 int sparse_attn_prefill(const void* q, const void* kv, const int32_t* S, int B, int n, int H, int Dqk, int Dv, int k,
                         float softmax_scale, tlsl_dtype dt, void* out, float* lse, void* workspace, size_t* ws_bytes,
                         hipStream_t stream) {
@@ -231,6 +260,53 @@ int dense_attn_prefill(const void* q, const void* kv, int B, int n, int H, int D
     // the sparse kernel with n slots per row and no index array: slot i is position i
     return launch_result(tlsl::launch_sparse_attn_prefill(s, q, kv, nullptr, B, n, n, softmax_scale, out, lse, stream),
                          "dense_attn_prefill");
+}
+
+int dsa_prefill(const void* qI, const float* q_scale, const void* kI, const float* k_scale, const float* wI, int HI,
+                int dI, tlsl_dtype idx_dt, const void* q, const void* kv, int H, int Dqk, int Dv, float softmax_scale,
+                tlsl_dtype attn_dt, int B, int n, int k, int32_t* S, void* out, float* lse, void* workspace,
+                size_t* ws_bytes, hipStream_t stream) {
+    int rc = check_indexer(idx_dt, qI, q_scale, kI, k_scale, wI, HI, dI, "dsa_prefill");
+    if (rc) return rc;
+    if (!q || !kv || !out) return fail(TLSL_ERR_NULL, "dsa_prefill: q, kv and out must be non-NULL");
+    if (B <= 0 || n <= 0 || k <= 0 || H <= 0) return fail(TLSL_ERR_SHAPE, "dsa_prefill: B, n, k and H must be positive");
+    if ((int64_t)B * n > (int64_t)1 << 30) return fail(TLSL_ERR_SHAPE, "dsa_prefill: B*n too large");
+    if (k > 4096) return fail(TLSL_ERR_UNSUPPORTED, "dsa_prefill: k=%d above the supported 4096", k);
+    if (attn_dt != TLSL_F32 && attn_dt != TLSL_BF16)
+        return fail(TLSL_ERR_UNSUPPORTED, "dsa_prefill: attention dtype %d not supported", attn_dt);
+    tlsl::AttnShape as{attn_dt, H, Dqk, Dv};
+    if (!tlsl::attn_supported(as))
+        return fail(TLSL_ERR_UNSUPPORTED, "dsa_prefill: attention (dtype %s, H=%d, Dqk=%d, Dv=%d) not built",
+                    dt_name(attn_dt), H, Dqk, Dv);
+    if (!(softmax_scale > 0.f) || !isfinite(softmax_scale))
+        return fail(TLSL_ERR_SHAPE, "dsa_prefill: softmax_scale must be positive and finite");
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || !aligned16(lse) || !aligned16(S))
+        return fail(TLSL_ERR_ALIGN, "dsa_prefill: pointers not 16-byte aligned");
+    // every row keeps all of its history when n <= k: the dense path gives the
+    // same result without the indexer; otherwise indexer, top-k and gather
+    const bool dense = n <= k;
+    const tlsl::IndexerShape is{idx_dt, HI, dI};
+    const tlsl::PrefillPlan plan = tlsl::plan_prefill(is, B, n, k);
+    const size_t s_bytes = S ? 0 : (((size_t)B * n * k * sizeof(int32_t) + 255) & ~(size_t)255);
+    const size_t need = dense ? 256 : plan.ws_bytes + s_bytes;  // never 0: NULL always means "size query"
+    rc = workspace_protocol(workspace, ws_bytes, need);
+    if (rc) return rc > 0 ? ok() : rc;
+    if (dense) {
+        if (S) {
+            const hipError_t e = tlsl::launch_fill_all_history(S, B, n, k, stream);
+            if (e != hipSuccess) return launch_result(e, "dsa_prefill");
+        }
+        return launch_result(tlsl::launch_sparse_attn_prefill(as, q, kv, nullptr, B, n, n, softmax_scale, out, lse,
+                                                              stream),
+                             "dsa_prefill");
+    }
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    int32_t* Sx = S ? S : reinterpret_cast<int32_t*>(ws + plan.ws_bytes);
+    const hipError_t e = tlsl::launch_index_prefill(is, qI, q_scale, kI, k_scale, wI, B, n, k, Sx, nullptr, ws, plan,
+                                                    stream);
+    if (e != hipSuccess) return launch_result(e, "dsa_prefill");
+    return launch_result(tlsl::launch_sparse_attn_prefill(as, q, kv, Sx, B, n, k, softmax_scale, out, lse, stream),
+                         "dsa_prefill");
 }
 
 int sparse_attn_decode(const void* q, const void* kv_cache, const int64_t* cu_seqlens, const int32_t* S, int B, int H,

@@ -25,6 +25,8 @@
 // XCD's L2.
 #include <math.h>
 
+#include <algorithm>
+
 #include "tlsl_device.h"
 #include "tlsl_internal.h"
 
@@ -627,6 +629,24 @@ static void dispatch_attn(const AttnShape& s, const AttnArgs& a, int rows, hipSt
         launch_attn_t<kBF16, 4, 2, 576, 512, DEC>(a, rows, st);
     else
         launch_attn_t<kF32, 1, 1, 80, 64, DEC>(a, rows, st);
+}
+
+// S[row, i] = i for i <= t, -1 above: the selection TopK(min(k, t+1)) makes
+// when every row keeps all of its history (t + 1 <= k)
+__global__ __launch_bounds__(256) void fill_all_history_kernel(int32_t* S, int n, int k, size_t total) {
+    for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
+        const int i = (int)(e % k);
+        const int t = (int)((e / k) % n);
+        S[e] = i <= t ? i : -1;
+    }
+}
+
+hipError_t launch_fill_all_history(int32_t* S, int B, int n, int k, hipStream_t st) {
+    const size_t total = (size_t)B * n * k;
+    const int grid = (int)std::min<size_t>((total + 255) / 256, (size_t)device_cu_count() * 8);
+    TLSL_TIMED_LAUNCH("fill_all_history_kernel", st,
+                      hipLaunchKernelGGL(fill_all_history_kernel, dim3(grid), dim3(256), 0, st, S, n, k, total));
+    return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn_prefill(const AttnShape& s, const void* q, const void* kv, const int32_t* S, int B,

@@ -60,6 +60,16 @@ TopkLayout topk_layout(int R, int k) {
 
 size_t topk_ws_bytes(int R, int k, int) { return topk_layout(R, k).bytes; }
 
+// ---- selection-quality diagnostics ----------------------------------------------
+// the teacher's top-m (int32 per slot), then topk_select's own workspace
+size_t selection_quality_ws_bytes(int R, int m, int max_len) {
+    return align256((size_t)R * m * sizeof(int32_t)) + topk_ws_bytes(R, m, max_len);
+}
+// the top-(k+1) positions and scores, then topk_select's own workspace
+size_t cutoff_margin_ws_bytes(int R, int k, int max_len) {
+    return 2 * align256((size_t)R * (k + 1) * sizeof(int32_t)) + topk_ws_bytes(R, k + 1, max_len);
+}
+
 // ---- sparse attention ---------------------------------------------------------
 bool attn_supported(const AttnShape& s) {
     if (s.dt == kBF16) return s.Dqk == 576 && s.Dv == 512 && s.H >= 1 && s.H <= 128;

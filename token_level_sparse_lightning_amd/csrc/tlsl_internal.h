@@ -68,6 +68,15 @@ hipError_t launch_topk_select(const float* scores, const int64_t* row_start,
                               const int32_t* row_len, int R, int k, int max_len, int32_t* S,
                               float* S_score, void* ws, hipStream_t st);
 
+// ---- selection-quality diagnostics ------------------------------------------------
+size_t selection_quality_ws_bytes(int R, int m, int max_len);
+size_t cutoff_margin_ws_bytes(int R, int k, int max_len);
+hipError_t launch_selection_quality(const float* teacher, const int64_t* row_start, const int32_t* row_len, int R,
+                                    const int32_t* S, int k, int m, int max_len, float* recall, float* mass,
+                                    void* ws, hipStream_t st);
+hipError_t launch_cutoff_margin(const float* scores, const int64_t* row_start, const int32_t* row_len, int R, int k,
+                                int max_len, float* margin, void* ws, hipStream_t st);
+
 // ---- indexer training step (sparse-stage loss and gradient) -----------------------
 hipError_t launch_indexer_kl(const void* q, const void* k, const float* w, const int32_t* S, const float* p,
                              int B, int n, int HI, int topk, float* loss, float* dq, float* dk, float* dw,
@@ -85,6 +94,7 @@ size_t attn_decode_ws_bytes(const AttnShape& s, int B, int k);
 hipError_t launch_sparse_attn_prefill(const AttnShape& s, const void* q, const void* kv,
                                       const int32_t* S, int B, int n, int k, float scale,
                                       void* out, float* lse, hipStream_t st);
+hipError_t launch_fill_all_history(int32_t* S, int B, int n, int k, hipStream_t st);
 hipError_t launch_sparse_attn_decode(const AttnShape& s, const void* q, const void* kv,
                                      const int64_t* cu, const int32_t* S, int B, int k,
                                      float scale, void* out, float* lse, void* ws,
