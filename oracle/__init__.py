@@ -59,6 +59,7 @@ def _load():
         lib.ora_indexer_kl.argtypes = [I, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P]
         lib.ora_indexer_kl_mag.argtypes = [I, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.ora_selection_quality.argtypes = [P, P, P, I, P, I, I, P, P]
+        lib.ora_rerank_rows.argtypes = [I, P, P, P, I, I, I, I, P, I, P, I, I, P, P]
         lib.ora_cutoff_margin.argtypes = [P, P, P, I, I, P]
         lib.ora_num_threads.restype = I
         _lib = lib
@@ -289,3 +290,35 @@ def cutoff_margin(scores, row_start, row_len, k):
     _check(lib.ora_cutoff_margin(_ptr(scores), _ptr(row_start), _ptr(row_len), R, int(k), _ptr(margin)),
            "cutoff_margin")
     return margin
+
+
+def rerank_rows(dt_fine, q, k_in, w, rows, C, k):
+    """Re-rank (DSA page section 2, the quantised-cache paragraph): the listed
+    rows' candidates C [nrows, kc] (positions; entries outside [0, t] skipped)
+    scored with eq.(1) on the fine inputs (f32 or bf16 storage), the min(k,
+    #candidates) best by (score desc, position asc), ascending, then -1.
+    Returns (S [nrows,k], S_score [nrows,k])."""
+    lib = _load()
+    q = _c(q)
+    k_in = _c(k_in)
+    w = _c(w, np.float32)
+    rows = _c(rows, np.int64)
+    C = _c(C, np.int32)
+    B, n, HI, DI = q.shape
+    nr, kc = C.shape
+    if len(rows) != nr:
+        raise ValueError("oracle rerank_rows: one candidate row per listed row")
+    S = np.empty((nr, k), np.int32)
+    Ss = np.empty((nr, k), np.float32)
+    _check(lib.ora_rerank_rows(dt_fine, _ptr(q), _ptr(k_in), _ptr(w), B, n, HI, DI, _ptr(rows), nr, _ptr(C), kc, k,
+                               _ptr(S), _ptr(Ss)), "rerank_rows")
+    return S, Ss
+
+
+def index_prefill_rerank_rows(dt_coarse, q_c, q_scale, k_c, k_scale, dt_fine, q_f, k_f, w, k, k_coarse, rows):
+    """Coarse recall then re-rank: C = TopK over the coarse inputs' scores with
+    budget k_coarse (eq.(1)-(2)), then the k best of C by the fine inputs'
+    scores.  Returns (S, S_score, C)."""
+    C, _, _, _ = index_prefill_rows(dt_coarse, q_c, q_scale, k_c, k_scale, w, k_coarse, rows)
+    S, Ss = rerank_rows(dt_fine, q_f, k_f, w, rows, C, k)
+    return S, Ss, C

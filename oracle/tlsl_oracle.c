@@ -639,6 +639,63 @@ int ora_indexer_kl_mag(int dt, const void *qI, const float *q_scale, const void 
     return 0;
 }
 
+/* ---- coarse recall, then re-rank (DSA page, section 2, the paragraph on the
+ * quantised key cache: recall a larger candidate set at FP8, then rank it with
+ * a higher-precision indexer) ----------------------------------------------
+ *
+ * For each listed row (flattened b*n + t) the candidates are the valid entries
+ * of C[r, 0..kc) (0 <= C <= t, each counted once); their scores are eq.(1) on
+ * the fine inputs (dt_fine), and the min(k, #candidates) best by (score desc,
+ * position asc) are written in ascending position order, then -1;
+ * S_score holds each slot's fine score (-inf for padding). */
+int ora_rerank_rows(int dt_fine, const void *qI, const void *kI, const float *wI, int B, int n,
+                    int HI, int DI, const int64_t *rows, int nrows, const int32_t *C, int kc, int k,
+                    int32_t *S, float *S_score)
+{
+    if (!qI || !kI || !wI || !rows || !C || !S || B <= 0 || n <= 0 || HI <= 0 || DI <= 0 || kc <= 0 ||
+        k <= 0 || dt_fine == ORA_FP8)
+        return -1;
+    if (!rows_ok(rows, nrows, (int64_t)B * n))
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; ++r) {
+        const int64_t row = rows[r], b = row / n, t = row % n;
+        double *q = malloc(sizeof(double) * (size_t)HI * DI);
+        double *w = malloc(sizeof(double) * (size_t)HI);
+        double *kk = malloc(sizeof(double) * (size_t)DI);
+        ora_cand *c = malloc(sizeof(ora_cand) * (size_t)kc);
+        char *seen = calloc((size_t)t + 1, 1);
+        load_token(dt_fine, qI, NULL, row, (int64_t)HI * DI, q);
+        for (int j = 0; j < HI; ++j)
+            w[j] = (double)wI[row * HI + j];
+        int nc = 0;
+        for (int i = 0; i < kc; ++i) {
+            const int32_t s = C[(int64_t)r * kc + i];
+            if (s < 0 || s > t || seen[s])
+                continue;
+            seen[s] = 1;
+            load_token(dt_fine, kI, NULL, b * n + s, DI, kk);
+            c[nc].score = (float)indexer_score(q, w, kk, HI, DI, NULL);
+            c[nc].pos = s;
+            ++nc;
+        }
+        const int K = nc < k ? nc : k;
+        qsort(c, (size_t)nc, sizeof(ora_cand), cmp_rank);
+        qsort(c, (size_t)K, sizeof(ora_cand), cmp_pos);
+        for (int i = 0; i < k; ++i) {
+            S[(int64_t)r * k + i] = i < K ? c[i].pos : -1;
+            if (S_score)
+                S_score[(int64_t)r * k + i] = i < K ? c[i].score : -INFINITY;
+        }
+        free(q);
+        free(w);
+        free(kk);
+        free(c);
+        free(seen);
+    }
+    return 0;
+}
+
 /* ---- selection-quality diagnostics (DSA page, sections 1.2 and 3.1) -----
  *
  * For row r, teacher masses a[0..L) (L = row_len[r], at row_start[r]) and a
