@@ -16,6 +16,8 @@ other rows of the path, each on its own workload (``extra``):
                        over all of its history), n=2048, H=128
   dispatch_2048        dsa_prefill at n = k = 2048 (dense path: every row keeps
                        all history) against index_prefill + sparse_attn_prefill
+  rerank_32768         index_prefill_rerank (fp8 recall k'=4096, bf16 re-rank to
+                       k=2048) at n=32768 against fp8 and bf16 index_prefill
   decode               one decode step of 64 ragged sequences
                        (L ~ U[16384,131072]): index_decode + topk_select +
                        sparse_attn_decode, tokens/s
@@ -270,6 +272,59 @@ def bench_dispatch(seed, steps, warmup):
                 speedup=ts.ev_med / td.ev_med)
 
 
+def _overlap(Sa, Sb, k):
+    """Mean fraction of Sb's selected positions that Sa also selects
+    (rows [R,k], ascending then -1); analysis of the bench's outputs."""
+    big = torch.iinfo(torch.int32).max
+    a = torch.where(Sa < 0, big, Sa).reshape(-1, k)
+    b = torch.where(Sb < 0, big, Sb).reshape(-1, k)
+    idx = torch.searchsorted(a.contiguous(), b.contiguous()).clamp(max=k - 1)
+    hit = (a.gather(1, idx) == b) & (b != big)
+    return float(hit.sum()) / float((b != big).sum())
+
+
+def bench_rerank(seed, steps, warmup):
+    """fp8 coarse recall (k' = 4096) then bf16 re-rank to k = 2048 at n=32768,
+    against the fp8 and the bf16 index_prefill at k = 2048 on the same values;
+    the selections' agreement with the bf16 one."""
+    n, HI, DI, k, kc = 32768, 64, 128, 2048, 4096
+    inp = synth.indexer_prefill(1, n, HI, DI, synth.DT_BF16, seed, planted=True, device=DEV)
+    q8, qs = synth.quantize_fp8_rows(inp.q.float(), 2)
+    k8, ks = synth.quantize_fp8_rows(inp.k.float(), 1)
+    S_rr = torch.empty((1, n, k), dtype=torch.int32, device=DEV)
+    S_8 = torch.empty_like(S_rr)
+    S_b = torch.empty_like(S_rr)
+    ws_rr = torch.empty(_rerank_ws_bytes(n, k, kc), dtype=torch.uint8, device=DEV)
+    ws_8 = torch.empty(tl.index_prefill_workspace_bytes(q8, k8, inp.w, k, qs, ks), dtype=torch.uint8, device=DEV)
+    ws_b = torch.empty(tl.index_prefill_workspace_bytes(inp.q, inp.k, inp.w, k), dtype=torch.uint8, device=DEV)
+    t_rr = time_calls(lambda: tl.index_prefill_rerank(q8, qs, k8, ks, inp.q, inp.k, inp.w, k, kc, S=S_rr,
+                                                      workspace=ws_rr), steps, warmup, kernel="rerank_kernel")
+    t_8 = time_calls(lambda: tl.index_prefill(q8, k8, inp.w, k, q_scale=qs, k_scale=ks, S=S_8, workspace=ws_8),
+                     steps, warmup)
+    t_b = time_calls(lambda: tl.index_prefill(inp.q, inp.k, inp.w, k, S=S_b, workspace=ws_b), steps, warmup)
+    torch.cuda.synchronize()
+    agree_rr, agree_8 = _overlap(S_rr, S_b, k), _overlap(S_8, S_b, k)
+    log(f"rerank n={n}: fp8 k'={kc} + bf16 re-rank {t_rr.ev_med:.3f} ms (rerank_kernel {t_rr.kernel_avg:.3f} ms), "
+        f"fp8 k={k} {t_8.ev_med:.3f} ms, bf16 k={k} {t_b.ev_med:.3f} ms; agreement with the bf16 selection: "
+        f"re-ranked {agree_rr:.5f}, fp8 {agree_8:.5f}")
+    del inp, q8, k8, S_rr, S_8, S_b, ws_rr, ws_8, ws_b
+    return dict(workload=f"coarse recall + re-rank: B=1, n={n}, H^I={HI}, d^I={DI}, fp8 k'={kc}, bf16 re-rank to "
+                         f"k={k}, planted keys",
+                rerank=t_rr.as_dict(), fp8_index_prefill=t_8.as_dict(), bf16_index_prefill=t_b.as_dict(),
+                agreement_with_bf16_selection={"reranked": agree_rr, "fp8_only": agree_8})
+
+
+def _rerank_ws_bytes(n, k, kc):
+    import ctypes
+    lib = tl.load()
+    size = ctypes.c_size_t(0)
+    d = ctypes.c_void_p(16)
+    rc = lib.index_prefill_rerank(d, d, d, d, d, d, d, 1, n, 64, 128, k, kc, d, None, None, None, ctypes.byref(size),
+                                  None)
+    assert rc == 0, lib.tlsl_last_error()
+    return size.value
+
+
 def bench_tiny(steps, warmup):
     """The tiny fp32 configuration (dyadic indexer inputs, exact scores):
     index_prefill and sparse_attn_prefill timed separately; report only."""
@@ -509,7 +564,7 @@ def recorded_traffic(kernel, workload):
 
 
 EXTRAS = ("attn_prefill_131072", "prefill_bf16_8192", "prefill_fp8_32768", "attn_prefill_32768",
-          "attn_dense_2048", "dispatch_2048", "decode", "train_8192", "tiny_f32_512")
+          "attn_dense_2048", "dispatch_2048", "rerank_32768", "decode", "train_8192", "tiny_f32_512")
 
 
 def main():
@@ -564,6 +619,9 @@ def main():
         torch.cuda.empty_cache()
     if "dispatch_2048" in want:
         extra["dispatch_2048"] = bench_dispatch(7, max(5, args.steps // 2), 2)
+        torch.cuda.empty_cache()
+    if "rerank_32768" in want:
+        extra["rerank_32768"] = bench_rerank(3, max(3, args.steps // 4), 1)
         torch.cuda.empty_cache()
     if "decode" in want:
         extra["decode"] = bench_decode(4, args.steps, args.warmup)

@@ -98,6 +98,33 @@ int index_prefill(const void* qI, const float* q_scale, const void* kI, const fl
                   hipStream_t stream);
 
 /*
+ * index_prefill_rerank -- coarse recall at fp8, then a high-precision re-rank
+ * (DSA page, section 2, the paragraph on the quantised key cache: fp8 shifts
+ * the order near the selection boundary; recall a larger candidate set, then
+ * rank it with a higher-precision indexer).  For every row t:
+ *     C_t = TopK over the fp8 inputs' scores, budget min(k_coarse, t+1)
+ *           (index_prefill on qI8/kI8 with their scales)
+ *     S_t = the min(k, |C_t|) best of C_t by the scores of the bf16 inputs
+ *           qI/kI (eq.(1), the same weights wI), ties to the lower position,
+ *           written in ascending position order, then -1.
+ * With k_coarse >= n this is index_prefill on the bf16 inputs, bit for bit;
+ * with k_coarse = k it keeps C_t.
+ *
+ *   qI8 [B,n,HI,dI] fp8 + q_scale [B,n];  kI8 [B,n,dI] fp8 + k_scale [B,n]
+ *   qI  [B,n,HI,dI] bf16;  kI [B,n,dI] bf16;  wI [B,n,HI] fp32
+ *   S [B,n,k] int32 out; S_score [B,n,k] fp32 out (optional): the bf16 scores
+ *   C [B,n,k_coarse] int32 out (optional): the candidates; when NULL they are
+ *     kept in the workspace
+ *   workspace: query protocol (index_prefill's for k_coarse, plus C if NULL).
+ * Supported: dI = 128, 1 <= HI <= 64, 1 <= k <= k_coarse <= 4096.
+ */
+int index_prefill_rerank(const void* qI8, const float* q_scale, const void* kI8,
+                         const float* k_scale, const void* qI, const void* kI, const float* wI,
+                         int B, int n, int HI, int dI, int k, int k_coarse, int32_t* S,
+                         float* S_score, int32_t* C, void* workspace, size_t* ws_bytes,
+                         hipStream_t stream);
+
+/*
  * index_decode -- Lightning Indexer score of each sequence's newest token
  * against its whole indexer key cache (DSA page, section 1.1 eq.(1); the decode
  * paragraph of section 2: one new query per step scans all cached K^I, which

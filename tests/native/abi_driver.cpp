@@ -53,6 +53,18 @@ int main() {
     EXPECT(index_prefill(odd, nullptr, P, nullptr, F, 1, 100, 64, 128, 16, TLSL_BF16, I32, F, P, &ws, nullptr), TLSL_ERR_ALIGN);
     EXPECT(index_prefill(P, nullptr, P, nullptr, F, 1 << 16, 1 << 15, 64, 128, 16, TLSL_BF16, I32, F, P, &ws, nullptr), TLSL_ERR_SHAPE);
 
+    // ---- index_prefill_rerank
+    EXPECT(index_prefill_rerank(P, F, P, F, P, P, F, 1, 100, 64, 128, 16, 64, I32, F, nullptr, nullptr, &need, nullptr),
+           TLSL_OK);
+    ws = need;
+    EXPECT(index_prefill_rerank(P, F, P, F, P, P, F, 1, 100, 64, 128, 16, 64, I32, F, nullptr, P, &ws, nullptr), TLSL_OK);
+    EXPECT(index_prefill_rerank(P, F, P, F, P, P, F, 1, 100, 64, 128, 65, 64, I32, F, nullptr, P, &ws, nullptr),
+           TLSL_ERR_SHAPE);
+    EXPECT(index_prefill_rerank(P, F, P, F, P, P, F, 1, 100, 64, 64, 16, 64, I32, F, nullptr, P, &ws, nullptr),
+           TLSL_ERR_UNSUPPORTED);
+    EXPECT(index_prefill_rerank(P, nullptr, P, F, P, P, F, 1, 100, 64, 128, 16, 64, I32, F, nullptr, P, &ws, nullptr),
+           TLSL_ERR_NULL);
+
     // ---- index_decode
     EXPECT(index_decode(P, F, P, F, F, I64, 4, 64, 128, 1000, TLSL_FP8_E4M3, F, nullptr, &ws, nullptr), TLSL_OK);
     if (ws != 0) { fprintf(stderr, "index_decode: nonzero workspace\n"); ++g_fail; }
@@ -135,12 +147,12 @@ int main() {
     EXPECT(sparse_attn_decode(P, P, I64, I32, 64, 128, 576, 512, 2048, sc, TLSL_BF16, P, F, nullptr, nullptr, nullptr), TLSL_ERR_NULL);
     if (strlen(tlsl_version()) == 0) ++g_fail;
 
-    // accepted calls: index_prefill, index_decode, topk_select, topk_select_noalloc (2),
+    // accepted calls: index_prefill, index_prefill_rerank, index_decode, topk_select, topk_select_noalloc (2),
     // indexer_loss_grad, dsa_prefill dense (fill + attention) and sparse (index +
     // attention), selection_quality, cutoff_margin, sparse_attn_prefill, dense_attn_prefill, sparse_attn_decode (the
     // last one's stand-in fails on purpose)
-    if (g_launches != 15) {
-        fprintf(stderr, "expected 15 launches, saw %d\n", g_launches);
+    if (g_launches != 16) {
+        fprintf(stderr, "expected 16 launches, saw %d\n", g_launches);
         ++g_fail;
     }
     if (g_fail) return 1;

@@ -21,6 +21,12 @@ hipError_t launch_index_prefill(const IndexerShape&, const void*, const float*, 
     ++g_launches;
     return hipSuccess;
 }
+hipError_t launch_index_prefill_rerank(const IndexerShape&, const void*, const float*, const void*, const float*,
+                                       const void*, const void*, const float*, int, int, int, int, int32_t*, float*,
+                                       int32_t*, void*, const PrefillPlan&, hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
 hipError_t launch_index_decode(const IndexerShape&, const void*, const float*, const void*, const float*,
                                const float*, const int64_t*, int, int, float*, hipStream_t) {
     ++g_launches;

@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     dsa_prefill,
     index_decode,
     index_prefill,
+    index_prefill_rerank,
     index_prefill_workspace_bytes,
     indexer_loss_grad,
     load,

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libtlsl.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 
-EXPORTS = ("index_prefill", "index_decode", "topk_select", "topk_select_noalloc", "sparse_attn_prefill",
+EXPORTS = ("index_prefill", "index_prefill_rerank", "index_decode", "topk_select", "topk_select_noalloc", "sparse_attn_prefill",
            "dense_attn_prefill", "dsa_prefill", "sparse_attn_decode", "indexer_loss_grad", "selection_quality", "cutoff_margin",
            "tlsl_last_error", "tlsl_version",
            # measurement aids (include/tlsl_measure.h)
@@ -53,10 +53,12 @@ def load():
     lib.indexer_loss_grad.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P]
     lib.dsa_prefill.argtypes = [P, P, P, P, P, I, I, I, P, P, I, I, I, F, I, I, I, I, P, P, P, P, SZ, P]
     lib.selection_quality.argtypes = [P, P, P, I, P, I, I, I, P, P, P, SZ, P]
+    lib.index_prefill_rerank.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, SZ, P]
     lib.cutoff_margin.argtypes = [P, P, P, I, I, I, P, P, SZ, P]
     for fn in ("index_prefill", "index_decode", "topk_select", "topk_select_noalloc", "sparse_attn_prefill",
                "dense_attn_prefill",
-               "sparse_attn_decode", "indexer_loss_grad", "dsa_prefill", "selection_quality", "cutoff_margin"):
+               "sparse_attn_decode", "indexer_loss_grad", "dsa_prefill", "selection_quality", "cutoff_margin",
+               "index_prefill_rerank"):
         getattr(lib, fn).restype = I
     lib.tlsl_last_error.restype = ctypes.c_char_p
     lib.tlsl_version.restype = ctypes.c_char_p
@@ -135,6 +137,27 @@ def index_prefill(qI, kI, wI, k, q_scale=None, k_scale=None, S=None, S_score=Non
                            ctypes.byref(size), _stream(stream))
     _check("index_prefill", rc)
     return S, S_score
+
+
+def index_prefill_rerank(qI8, q_scale, kI8, k_scale, qI, kI, wI, k, k_coarse, S=None, S_score=None,
+                         want_scores=False, C=None, want_C=False, workspace=None, stream=None):
+    """fp8 coarse recall (budget k_coarse), then the k best candidates by the
+    bf16 inputs' scores: returns (S [B,n,k], S_score or None, C or None)."""
+    lib = load()
+    for t, nm in ((qI8, "qI8"), (kI8, "kI8"), (qI, "qI"), (kI, "kI"), (wI, "wI")):
+        _need(t, nm)
+    B, n, HI, DI = qI.shape
+    dev = qI.device
+    if S is None:
+        S = torch.empty((B, n, k), dtype=torch.int32, device=dev)
+    if S_score is None and want_scores:
+        S_score = torch.empty((B, n, k), dtype=torch.float32, device=dev)
+    if C is None and want_C:
+        C = torch.empty((B, n, k_coarse), dtype=torch.int32, device=dev)
+    args = [_ptr(qI8), _ptr(q_scale), _ptr(kI8), _ptr(k_scale), _ptr(qI), _ptr(kI), _ptr(wI), B, n, HI, DI, int(k),
+            int(k_coarse), _ptr(S), _ptr(S_score), _ptr(C)]
+    _with_workspace("index_prefill_rerank", args, dev, workspace, stream)
+    return S, S_score, C
 
 
 def index_decode(qI, kI_cache, wI, cu_seqlens, max_len, q_scale=None, k_scale=None,

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtlsl.so")
 
-SOURCES = ["abi.cpp", "plan.cpp", "indexer.hip", "topk.hip", "attn.hip", "train.hip", "diag.hip", "measure.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "indexer.hip", "topk.hip", "attn.hip", "train.hip", "diag.hip", "rerank.hip", "measure.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -39,7 +39,8 @@ HIPCC_FLAGS = [
 # indexer is scheduled for instruction-level parallelism (measured 2% faster on
 # the fp8 prefill scoring kernel, neutral elsewhere)
 SOURCE_FLAGS = {"measure.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-                "indexer.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+                "indexer.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+                "rerank.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def _hipcc() -> str:

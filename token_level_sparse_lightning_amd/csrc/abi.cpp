@@ -125,6 +125,31 @@ int index_prefill(const void* qI, const float* q_scale, const void* kI, const fl
                          "index_prefill");
 }
 
+int index_prefill_rerank(const void* qI8, const float* q_scale, const void* kI8, const float* k_scale, const void* qI,
+                         const void* kI, const float* wI, int B, int n, int HI, int dI, int k, int k_coarse, int32_t* S,
+                         float* S_score, int32_t* C, void* workspace, size_t* ws_bytes, hipStream_t stream) {
+    int rc = check_indexer(TLSL_FP8_E4M3, qI8, q_scale, kI8, k_scale, wI, HI, dI, "index_prefill_rerank");
+    if (rc) return rc;
+    if (!qI || !kI || !S) return fail(TLSL_ERR_NULL, "index_prefill_rerank: qI, kI and S must be non-NULL");
+    if (dI != 128) return fail(TLSL_ERR_UNSUPPORTED, "index_prefill_rerank: dI=%d not built (128)", dI);
+    if (B <= 0 || n <= 0) return fail(TLSL_ERR_SHAPE, "index_prefill_rerank: B=%d and n=%d must be positive", B, n);
+    if (k <= 0 || k_coarse < k) return fail(TLSL_ERR_SHAPE, "index_prefill_rerank: need 1 <= k <= k_coarse");
+    if (k_coarse > 4096) return fail(TLSL_ERR_UNSUPPORTED, "index_prefill_rerank: k_coarse=%d above the supported 4096",
+                                     k_coarse);
+    if ((int64_t)B * n > (int64_t)1 << 30) return fail(TLSL_ERR_SHAPE, "index_prefill_rerank: B*n too large");
+    if (!aligned16(qI) || !aligned16(kI) || !aligned16(S) || !aligned16(S_score) || !aligned16(C))
+        return fail(TLSL_ERR_ALIGN, "index_prefill_rerank: pointers not 16-byte aligned");
+    const tlsl::IndexerShape coarse{TLSL_FP8_E4M3, HI, dI};
+    const tlsl::PrefillPlan plan = tlsl::plan_prefill(coarse, B, n, k_coarse);
+    const size_t c_bytes = C ? 0 : (((size_t)B * n * k_coarse * sizeof(int32_t) + 255) & ~(size_t)255);
+    rc = workspace_protocol(workspace, ws_bytes, plan.ws_bytes + c_bytes);
+    if (rc) return rc > 0 ? ok() : rc;
+    int32_t* Cx = C ? C : reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) + plan.ws_bytes);
+    return launch_result(tlsl::launch_index_prefill_rerank(coarse, qI8, q_scale, kI8, k_scale, qI, kI, wI, B, n, k,
+                                                           k_coarse, S, S_score, Cx, workspace, plan, stream),
+                         "index_prefill_rerank");
+}
+
 int index_decode(const void* qI, const float* q_scale, const void* kI_cache, const float* k_scale, const float* wI,
                  const int64_t* cu_seqlens, int B, int HI, int dI, int max_len, tlsl_dtype dt, float* scores,
                  void* workspace, size_t* ws_bytes, hipStream_t stream) {

@@ -402,11 +402,9 @@ __global__ __launch_bounds__(FIN_NT) void prefill_finalize_kernel(FinalizeArgs a
     // i % FIN_NT as its (i / FIN_NT)-th item: one coalesced read of the buffer
     // gives both the score keys for the selection and the positions for S.
     constexpr int SEG = (CAPMAX + FIN_NT - 1) / FIN_NT;
-    constexpr int NW = FIN_NT / 64;
-    constexpr int NE = SEG * NW;  // (item, wave) groups, in candidate order
     __shared__ SelectSmem sel;
-    __shared__ int gcnt[2][NE];
-    const int tid = threadIdx.x, w = tid >> 6;
+    __shared__ int gcnt[2][SEG * (FIN_NT / 64)];
+    const int tid = threadIdx.x;
     const int row = blockIdx.x;
     const int t = row % a.n;
     const int K = min(a.topk, t + 1);
@@ -428,80 +426,8 @@ __global__ __launch_bounds__(FIN_NT) void prefill_finalize_kernel(FinalizeArgs a
         key[u] = score_key(__uint_as_float(e[u].x));
         pos[u] = (int)e[u].y;
     }
-    // every candidate is kept when there are exactly K of them
-    const bool all = cnt == K;
-    uint32_t T = 0u;  // key of the K-th largest candidate
-    int gt = cnt;     // candidates with a key above T
-    if (!all) {
-        const auto each = [&](auto&& f) {
-#pragma unroll
-            for (int u = 0; u < SEG; ++u)
-                if (tid + u * FIN_NT < cnt) f(key[u]);
-        };
-        T = block_select_each<FIN_NT>(K, each, sel, &gt, true);
-    }
-    const int need_ties = K - gt;
-    // Ordered output: selected are every key above T and the first need_ties
-    // keys equal to T in position order.  Counts of both kinds per (item,
-    // wave) group, scanned in candidate order, give each candidate's slot.
-#pragma unroll
-    for (int u = 0; u < SEG; ++u) {
-        const bool ok = tid + u * FIN_NT < cnt;
-        const uint64_t mg = ballot(ok && (all || key[u] > T));
-        const uint64_t mt = ballot(ok && !all && key[u] == T);
-        if (lane_id() == 0) {
-            gcnt[0][u * NW + w] = __popcll(mg);
-            gcnt[1][u * NW + w] = __popcll(mt);
-        }
-    }
-    __syncthreads();
-    if (w == 0) {
-        // exclusive scan of the NE group counts by the first wave
-        constexpr int PER = (NE + 63) / 64;
-        const int l = lane_id();
-        int cg[PER], ct[PER], sg = 0, st = 0;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int e = l * PER + j;
-            cg[j] = e < NE ? gcnt[0][e] : 0;
-            ct[j] = e < NE ? gcnt[1][e] : 0;
-            sg += cg[j];
-            st += ct[j];
-        }
-        int eg = wave_incl_scan(sg) - sg, et = wave_incl_scan(st) - st;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int e = l * PER + j;
-            if (e < NE) {
-                gcnt[0][e] = eg;
-                gcnt[1][e] = et;
-            }
-            eg += cg[j];
-            et += ct[j];
-        }
-    }
-    __syncthreads();
-    int32_t* Srow = a.S + (size_t)row * a.topk;
-    float* Ssrow = a.Ss ? a.Ss + (size_t)row * a.topk : nullptr;
-#pragma unroll
-    for (int u = 0; u < SEG; ++u) {
-        if (u * FIN_NT >= cnt) break;
-        const bool ok = tid + u * FIN_NT < cnt;
-        const bool isg = ok && (all || key[u] > T);
-        const bool ist = ok && !all && key[u] == T;
-        const uint64_t mg = ballot(isg), mt = ballot(ist);
-        const int rg = gcnt[0][u * NW + w] + rank_below(mg);  // keys above T before this one
-        const int rt = gcnt[1][u * NW + w] + rank_below(mt);  // keys equal to T before this one
-        if (isg || (ist && rt < need_ties)) {
-            const int slot = rg + min(rt, need_ties);
-            Srow[slot] = pos[u];
-            if (Ssrow) Ssrow[slot] = key_score(key[u]);
-        }
-    }
-    for (int i = K + tid; i < a.topk; i += FIN_NT) {
-        Srow[i] = -1;
-        if (Ssrow) Ssrow[i] = -INFINITY;
-    }
+    select_ordered<FIN_NT, SEG>(key, pos, cnt, K, a.topk, a.S + (size_t)row * a.topk,
+                                a.Ss ? a.Ss + (size_t)row * a.topk : nullptr, sel, gcnt);
 }
 
 // ---------------------------------------------------------------------------

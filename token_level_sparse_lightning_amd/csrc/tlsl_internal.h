@@ -47,6 +47,11 @@ hipError_t launch_index_prefill(const IndexerShape& s, const void* q, const floa
                                 int n, int topk, int32_t* S, float* S_score, void* ws,
                                 const PrefillPlan& plan, hipStream_t st);
 
+hipError_t launch_index_prefill_rerank(const IndexerShape& coarse, const void* q8, const float* q_scale,
+                                       const void* k8, const float* k_scale, const void* qf, const void* kf,
+                                       const float* w, int B, int n, int topk, int kc, int32_t* S, float* S_score,
+                                       int32_t* C, void* ws, const PrefillPlan& plan, hipStream_t st);
+
 hipError_t launch_index_decode(const IndexerShape& s, const void* q, const float* q_scale,
                                const void* kc, const float* k_scale, const float* w,
                                const int64_t* cu, int B, int max_len, float* scores,

@@ -122,6 +122,99 @@ __device__ uint32_t block_select_each(int need, Each each, SelectSmem& sm, int* 
     return T;
 }
 
+// ---------------------------------------------------------------------------
+// Exact top-K of `cnt` candidates held in registers, written in candidate
+// order.  Candidate i (0 <= i < cnt) is item i / NT of thread i % NT, with its
+// order-preserving score key and its position; candidates are in ascending
+// position order, so "the lower position wins a tie" is "the earlier
+// candidate wins".  Writes the K = min(k, ...) selected positions to S[0..K)
+// (ascending), their scores to Ss (optional), then -1 / -inf up to S[topk).
+// All NT threads call it; requires K <= cnt.
+//
+// The K-th largest key T comes from the register-visiting select; every key
+// above T and the first K - gt keys equal to T are selected.  Per (item,
+// wave) group the counts of both kinds, scanned in candidate order by the
+// first wave, and each lane's rank inside its wave's ballot give every
+// selected candidate its slot.
+// ---------------------------------------------------------------------------
+template <int NT, int SEG>
+__device__ void select_ordered(const uint32_t (&key)[SEG], const int (&pos)[SEG], int cnt, int K, int topk,
+                               int32_t* __restrict__ Srow, float* __restrict__ Ssrow, SelectSmem& sel,
+                               int (&gcnt)[2][SEG * (NT / 64)]) {
+    constexpr int NW = NT / 64;
+    constexpr int NE = SEG * NW;  // (item, wave) groups, in candidate order
+    const int tid = threadIdx.x, w = tid >> 6;
+    // every candidate is kept when there are exactly K of them
+    const bool all = cnt == K;
+    uint32_t T = 0u;  // key of the K-th largest candidate
+    int gt = cnt;     // candidates with a key above T
+    if (!all) {
+        const auto each = [&](auto&& f) {
+#pragma unroll
+            for (int u = 0; u < SEG; ++u)
+                if (tid + u * NT < cnt) f(key[u]);
+        };
+        T = block_select_each<NT>(K, each, sel, &gt, true);
+    }
+    const int need_ties = K - gt;
+#pragma unroll
+    for (int u = 0; u < SEG; ++u) {
+        const bool ok = tid + u * NT < cnt;
+        const uint64_t mg = ballot(ok && (all || key[u] > T));
+        const uint64_t mt = ballot(ok && !all && key[u] == T);
+        if (lane_id() == 0) {
+            gcnt[0][u * NW + w] = __popcll(mg);
+            gcnt[1][u * NW + w] = __popcll(mt);
+        }
+    }
+    __syncthreads();
+    if (w == 0) {
+        // exclusive scan of the NE group counts by the first wave
+        constexpr int PER = (NE + 63) / 64;
+        const int l = lane_id();
+        int cg[PER], ct[PER], sg = 0, st = 0;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int e = l * PER + j;
+            cg[j] = e < NE ? gcnt[0][e] : 0;
+            ct[j] = e < NE ? gcnt[1][e] : 0;
+            sg += cg[j];
+            st += ct[j];
+        }
+        int eg = wave_incl_scan(sg) - sg, et = wave_incl_scan(st) - st;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int e = l * PER + j;
+            if (e < NE) {
+                gcnt[0][e] = eg;
+                gcnt[1][e] = et;
+            }
+            eg += cg[j];
+            et += ct[j];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < SEG; ++u) {
+        if (u * NT >= cnt) break;
+        const bool ok = tid + u * NT < cnt;
+        const bool isg = ok && (all || key[u] > T);
+        const bool ist = ok && !all && key[u] == T;
+        const uint64_t mg = ballot(isg), mt = ballot(ist);
+        const int rg = gcnt[0][u * NW + w] + rank_below(mg);  // keys above T before this one
+        const int rt = gcnt[1][u * NW + w] + rank_below(mt);  // keys equal to T before this one
+        if (isg || (ist && rt < need_ties)) {
+            const int slot = rg + min(rt, need_ties);
+            Srow[slot] = pos[u];
+            if (Ssrow) Ssrow[slot] = key_score(key[u]);
+        }
+    }
+    for (int i = K + tid; i < topk; i += NT) {
+        Srow[i] = -1;
+        if (Ssrow) Ssrow[i] = -INFINITY;
+    }
+}
+
 // Keys in workgroup-visible memory: key_of(i, &valid) for i < cnt, read by
 // thread i % NT.
 template <int NT, class KeyFn>
