@@ -63,6 +63,11 @@ constexpr int PF_WAVES = 8;
 constexpr int PF_NT = PF_WAVES * 64;
 constexpr int PF_RBUF = 512;      // per-query LDS buffer of sample scores
 constexpr float PF_SIGMA = 4.0f;  // safety margin of the sample threshold, in standard deviations
+// LDS scratch of one wave for the fp8 linear-part rows (the largest
+// Idx<kFP8, HB, 128>::LIN_SCRATCH); other input types need none
+constexpr int LIN_SCR = 8 * 128 + 8 * 4;
+template <int DT>
+constexpr int lin_scr_bytes() { return DT == kFP8 ? LIN_SCR : 16; }
 
 struct PrefillArgs {
     const unsigned char* q;
@@ -149,6 +154,33 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
         const float wmul = (DT == kFP8) ? a.q_scale[row] : 1.f;
         I::load_query(a.q + row * (size_t)a.HI * KT::ROWB, a.w + row * a.HI, wmul, a.HI, qv[i], qf[i], wv[i]);
     }
+    // fp8: the linear-part rows of the wave's queries (slot i = query i), built
+    // in the queries' sample buffers, which are free until the sample pass
+    uint4 ql[NCH];
+    float ls[2][2];
+    if constexpr (DT == kFP8) {
+        static_assert(I::LIN_SCRATCH <= PF_RBUF * (int)sizeof(float), "linear-part scratch fits a sample buffer");
+#pragma unroll
+        for (int i = 0; i < QW; ++i) {
+            const size_t row = tok0 + (qv[i] ? tq[i] : 0);
+            I::prep_lin(qf[i], a.w + row * a.HI, a.q_scale[row], a.HI, qv[i],
+                        reinterpret_cast<unsigned char*>(rbuf[wv_id * QW + i]));
+        }
+        wave_lds_fence();
+        I::load_lin(reinterpret_cast<const unsigned char*>(rbuf[wv_id * QW]),
+                    QW > 1 ? reinterpret_cast<const unsigned char*>(rbuf[wv_id * QW + QW - 1]) : nullptr, ql, ls);
+        wave_lds_fence();
+    }
+    // scores of query i for a subtile whose key fragments are kfx (fp8: lin
+    // holds the subtile's linear-part products)
+    auto score_q = [&](int i, const uint4 (&kfx)[4][NCH], const v4f (&lin)[4]) -> float {
+        if constexpr (DT == kFP8) {
+            if (i == 0) return I::template score_lin<0>(qf[0], wv[0], kfx, lin, ls[0]);
+            return I::template score_lin<1>(qf[QW - 1], wv[QW - 1], kfx, lin, ls[1]);
+        } else {
+            return I::score(qf[i], wv[i], kfx);
+        }
+    };
 
     // cooperative copy of 64 key rows (row r <- key key_of(r), clamped) into LDS
     auto copy_rows = [&](unsigned char* dst, int key0, int kstep) {
@@ -207,10 +239,12 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
             frag_from_lds(ktile[cur], kf);
             const int s = (js * 64 + l) * a.stride;
             const float ks = (DT == kFP8) ? a.k_scale[tok0 + min(s, a.n - 1)] : 1.f;
+            v4f slin[4];
+            if constexpr (DT == kFP8) I::lin_products(ql, kf, slin);
 #pragma unroll
             for (int i = 0; i < QW; ++i) {
                 if (rneed[i] == 0 || js * 64 * a.stride > tq[i]) continue;
-                float sc = I::score(qf[i], wv[i], kf);
+                float sc = score_q(i, kf, slin);
                 if (DT == kFP8) sc *= ks;
                 const bool ok = s <= tq[i] && sc >= rth[i];
                 const uint64_t m = ballot(ok);
@@ -285,6 +319,7 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
     };
     float tpart[3];
     v4f tlast[HB];
+    float tl0 = 0.f, tl1 = 0.f;  // fp8: the deferred query's linear rows of its last key block
     float tks = 1.f;
     int ts = 0;
     bool tpend = false;
@@ -319,7 +354,9 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
         size_t tidx = 0;
         uint2 tval = make_uint2(0, 0);
         if (tpend) {
-            float sc = I::score_tail(wv[QW - 1], tpart, tlast);
+            float sc;
+            if constexpr (DT == kFP8) sc = I::score_tail_lin(wv[QW - 1], tpart, tlast, tl0, tl1, ls[QW - 1]);
+            else sc = I::score_tail(wv[QW - 1], tpart, tlast);
             if (DT == kFP8) sc *= tks;
             select(QW - 1, sc, ts, tst, tidx, tval);
         }
@@ -329,16 +366,24 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
         bool cst[QW];
         size_t cidx[QW];
         uint2 cval[QW];
+        v4f lin[4];
+        if constexpr (DT == kFP8) I::lin_products(ql, kf, lin);
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
             cst[i] = false;
             if (!qv[i] || j * 64 > tq[i]) continue;
             if (i < QW - 1) {
-                float sc = I::score(qf[i], wv[i], kf);
+                float sc = score_q(i, kf, lin);
                 if (DT == kFP8) sc *= ks;
                 select(i, sc, s, cst[i], cidx[i], cval[i]);
             } else {
-                I::score_head(qf[i], wv[i], kf, tpart, tlast);
+                if constexpr (DT == kFP8) {
+                    I::template score_head_lin<QW - 1>(qf[i], wv[i], kf, lin, ls[QW - 1], tpart, tlast);
+                    tl0 = lin[3][2 * (QW - 1)];
+                    tl1 = lin[3][2 * (QW - 1) + 1];
+                } else {
+                    I::score_head(qf[i], wv[i], kf, tpart, tlast);
+                }
                 ts = s;
                 tks = ks;
                 tpend = true;
@@ -368,7 +413,9 @@ __global__ __launch_bounds__(PF_NT, 1) void prefill_score_kernel(PrefillArgs a) 
         bool tst;
         size_t tidx;
         uint2 tval;
-        float sc = I::score_tail(wv[QW - 1], tpart, tlast);
+        float sc;
+        if constexpr (DT == kFP8) sc = I::score_tail_lin(wv[QW - 1], tpart, tlast, tl0, tl1, ls[QW - 1]);
+        else sc = I::score_tail(wv[QW - 1], tpart, tlast);
         if (DT == kFP8) sc *= tks;
         select(QW - 1, sc, ts, tst, tidx, tval);
         if (tst) a.buf[tidx] = tval;
@@ -454,7 +501,7 @@ struct FallbackArgs {
 // main pass, so the scores are bit-identical to it).
 template <int DT, int HB, int DI>
 __device__ __forceinline__ void fallback_rescore(const FallbackArgs& a, int row, int j0, int j1, int jstep,
-                                                 float* sc) {
+                                                 float* sc, unsigned char* lscr) {
     using I = Idx<DT, HB, DI>;
     constexpr int NCH = I::NCH;
     const int l = lane_id();
@@ -464,11 +511,27 @@ __device__ __forceinline__ void fallback_rescore(const FallbackArgs& a, int row,
     float wv[HB][4];
     const float wmul = (DT == kFP8) ? a.q_scale[row] : 1.f;
     I::load_query(a.q + (size_t)row * a.HI * I::ROWB, a.w + (size_t)row * a.HI, wmul, a.HI, true, qf, wv);
+    // fp8: the row's linear-part rows in slot 0 (lscr: the wave's LDS scratch)
+    uint4 ql[NCH];
+    float ls[2][2];
+    if constexpr (DT == kFP8) {
+        I::prep_lin(qf, a.w + (size_t)row * a.HI, wmul, a.HI, true, lscr);
+        wave_lds_fence();
+        I::load_lin(lscr, nullptr, ql, ls);
+        wave_lds_fence();
+    }
     const unsigned char* kb_base = a.k + tok0 * I::ROWB;
     for (int j = j0; j < j1 && j * 64 <= t; j += jstep) {
         uint4 kf[4][NCH];
         I::load_keys_global(kb_base, j * 64, t, kf);
-        float s = I::score(qf, wv, kf);
+        float s;
+        if constexpr (DT == kFP8) {
+            v4f lin[4];
+            I::lin_products(ql, kf, lin);
+            s = I::template score_lin<0>(qf, wv, kf, lin, ls[0]);
+        } else {
+            s = I::score(qf, wv, kf);
+        }
         const int key = j * 64 + l;
         if (DT == kFP8) s *= a.k_scale[tok0 + min(key, t)];
         if (key <= t) sc[key] = s;
@@ -488,11 +551,13 @@ __global__ __launch_bounds__(FBS_NT) void prefill_fallback_score_kernel(Fallback
     const int nfb = min(*a.fb_count, fb_rows);
     const int nch = (a.n + FBS_CHUNK - 1) / FBS_CHUNK;
     const int w = threadIdx.x >> 6;
+    __shared__ __align__(16) unsigned char lscr[FBS_NT / 64][lin_scr_bytes<DT>()];
     for (int item = blockIdx.x; item < nfb * nch; item += gridDim.x) {
         const int i = item / nch, c = item - i * nch;
         const int row = a.fb_list[i];
         constexpr int SUB = FBS_CHUNK / 64;
-        fallback_rescore<DT, HB, DI>(a, row, c * SUB + w, (c + 1) * SUB, FBS_NT / 64, a.scratch + (size_t)i * a.n);
+        fallback_rescore<DT, HB, DI>(a, row, c * SUB + w, (c + 1) * SUB, FBS_NT / 64, a.scratch + (size_t)i * a.n,
+                                     lscr[w]);
     }
 }
 
@@ -501,13 +566,14 @@ __global__ __launch_bounds__(FBS_NT) void prefill_fallback_score_kernel(Fallback
 template <int DT, int HB, int DI>
 __global__ __launch_bounds__(FB_NT) void prefill_fallback_kernel(FallbackArgs a) {
     __shared__ TopkSmem sm;
+    __shared__ __align__(16) unsigned char lscr[FB_NT / 64][lin_scr_bytes<DT>()];
     const int nfb = *a.fb_count;
     const int w = threadIdx.x >> 6;
     float* sc = a.scratch + (size_t)blockIdx.x * a.n;
     for (int it = blockIdx.x; it < nfb; it += gridDim.x) {
         const int row = a.fb_list[it];
         const int t = row % a.n;
-        if (it >= (int)gridDim.x) fallback_rescore<DT, HB, DI>(a, row, w, 1 << 30, FB_NT / 64, sc);
+        if (it >= (int)gridDim.x) fallback_rescore<DT, HB, DI>(a, row, w, 1 << 30, FB_NT / 64, sc, lscr[w]);
         __threadfence();
         __syncthreads();
         __threadfence();
@@ -535,10 +601,27 @@ __global__ __launch_bounds__(DEC_NT) void decode_score_kernel(const unsigned cha
     const int L = (int)(cu[b + 1] - start);
     if ((int64_t)blockIdx.y * DEC_CHUNK >= L) return;
     const int wv_id = threadIdx.x >> 6, l = lane_id();
+    __shared__ __align__(16) unsigned char lscr[DEC_NT / 64][lin_scr_bytes<DT>()];
     uint4 qf[HB][NCH];
     float wv[HB][4];
     const float wmul = (DT == kFP8) ? q_scale[b] : 1.f;
     I::load_query(q + (size_t)b * HI * I::ROWB, w + (size_t)b * HI, wmul, HI, true, qf, wv);
+    uint4 ql[NCH];
+    float ls[2][2];
+    if constexpr (DT == kFP8) {
+        I::prep_lin(qf, w + (size_t)b * HI, wmul, HI, true, lscr[wv_id]);
+        wave_lds_fence();
+        I::load_lin(lscr[wv_id], nullptr, ql, ls);
+    }
+    auto score_sub = [&](const uint4 (&kfx)[4][NCH]) -> float {
+        if constexpr (DT == kFP8) {
+            v4f lin[4];
+            I::lin_products(ql, kfx, lin);
+            return I::template score_lin<0>(qf, wv, kfx, lin, ls[0]);
+        } else {
+            return I::score(qf, wv, kfx);
+        }
+    };
     const unsigned char* kb_base = kc + (size_t)start * I::ROWB;
     constexpr int STEP = 64 * (DEC_NT / 64);
     // chunks blockIdx.y, + gridDim.y, ...: a sequence longer than the launch
@@ -554,7 +637,7 @@ __global__ __launch_bounds__(DEC_NT) void decode_score_kernel(const unsigned cha
             const int j1 = j0 + STEP;
             if (j1 < end) I::load_keys_global(kb_base, j1, L - 1, kf[1]);
             {
-                float s = I::score(qf, wv, kf[0]);
+                float s = score_sub(kf[0]);
                 const int key = j0 + l;
                 if (DT == kFP8) s *= k_scale[start + min(key, L - 1)];
                 if (key < L) scores[start + key] = s;
@@ -562,7 +645,7 @@ __global__ __launch_bounds__(DEC_NT) void decode_score_kernel(const unsigned cha
             if (j1 >= end) break;
             if (j1 + STEP < end) I::load_keys_global(kb_base, j1 + STEP, L - 1, kf[0]);
             {
-                float s = I::score(qf, wv, kf[1]);
+                float s = score_sub(kf[1]);
                 const int key = j1 + l;
                 if (DT == kFP8) s *= k_scale[start + min(key, L - 1)];
                 if (key < L) scores[start + key] = s;
@@ -585,7 +668,9 @@ constexpr int DEC2_MAXB = 4096;
 // (written at the end of each sequence run or when full).  Stored per subtile
 // in between the key loads, the 256-byte score stores cost 22 of 135 us at
 // 64 sequences; staged, about half of that.
-constexpr size_t DEC2_LDS_BUDGET = 78 * 1024;  // per workgroup (two resident per CU)
+// dynamic LDS per workgroup: with the static part (the fp8 linear-part
+// scratch, 4.2 KB) two workgroups stay resident per CU (160 KB)
+constexpr size_t DEC2_LDS_BUDGET = 74 * 1024;
 __host__ __device__ constexpr size_t dec2_off_sstart(int B) { return ((size_t)(B + 1) * 4 + 7) & ~(size_t)7; }
 __host__ __device__ constexpr size_t dec2_off_stage(int B) {
     return (dec2_off_sstart(B) + (size_t)(B + 1) * 8 + 15) & ~(size_t)15;
@@ -654,6 +739,9 @@ __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned cha
 
     uint4 qf[HB][NCH];
     float wv[HB][4];
+    uint4 ql[NCH];  // fp8: linear-part rows of the segment's query (slot 0)
+    float ls[2][2];
+    __shared__ __align__(16) unsigned char lscr[NWV][lin_scr_bytes<DT>()];
     uint4 kf[2][4][NCH];
     float ksc[2];
     // the wave's subtiles are g0+wv_id, +NWV, ...; they are walked one sequence
@@ -672,6 +760,12 @@ __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned cha
         const unsigned char* kbase = kc + (size_t)start * I::ROWB;
         const float wmul = (DT == kFP8) ? q_scale[b] : 1.f;
         I::load_query(q + (size_t)b * HI * I::ROWB, w + (size_t)b * HI, wmul, HI, true, qf, wv);
+        if constexpr (DT == kFP8) {
+            wave_lds_fence();  // the previous segment's reads of the scratch are done
+            I::prep_lin(qf, w + (size_t)b * HI, wmul, HI, true, lscr[wv_id]);
+            wave_lds_fence();
+            I::load_lin(lscr[wv_id], nullptr, ql, ls);
+        }
         int key0 = (g - pre[b]) * 64;
         auto fetch = [&](int k0, uint4 (&kf_)[4][NCH], float& ks_) {
             I::load_keys_global(kbase, min(k0, L - 1), L - 1, kf_);
@@ -688,7 +782,9 @@ __global__ __launch_bounds__(DEC2_NT) void decode_scan_kernel(const unsigned cha
         };
         auto step = [&](const uint4 (&cur)[4][NCH], float ks, uint4 (&ahead)[4][NCH], float& ks_ahead) {
             fetch(key0 + 64 * NWV, ahead, ks_ahead);
-            const float s = I::score_lean(qf, wv, cur) * ks;
+            float s;
+            if constexpr (DT == kFP8) s = I::score_lean_lin(qf, wv, cur, ql, ls[0]) * ks;
+            else s = I::score_lean(qf, wv, cur) * ks;
             if (scap == 0) {
                 if (g - g0 < stage_sub) stage[(size_t)(g - g0) * 64 + l] = s;
                 else if (key0 + l < L) scores[start + key0 + l] = s;

@@ -10,6 +10,7 @@ namespace tlsl {
 
 constexpr int kF32 = 0, kBF16 = 1, kFP8 = 2;
 
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
