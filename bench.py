@@ -542,7 +542,7 @@ def cpu_baseline(inp, k, n, target_s=15.0):
 # bytes exactly).  The figures hold only for the kernel sources they were
 # taken on: when the hash of those sources differs, traffic is reported as
 # null.  Commands and readings: profiles/prefill_score_kernel_fp8_n131072.md.
-TRAFFIC_SOURCES = ("indexer.hip", "tlsl_device.h", "tlsl_internal.h", "topk_common.h")
+TRAFFIC_SOURCES = ("indexer.hip", "idx_tile.h", "tlsl_device.h", "tlsl_internal.h", "topk_common.h")
 TRAFFIC = {}
 
 
