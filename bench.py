@@ -543,7 +543,17 @@ def cpu_baseline(inp, k, n, target_s=15.0):
 # taken on: when the hash of those sources differs, traffic is reported as
 # null.  Commands and readings: profiles/prefill_score_kernel_fp8_n131072.md.
 TRAFFIC_SOURCES = ("indexer.hip", "idx_tile.h", "tlsl_device.h", "tlsl_internal.h", "topk_common.h")
-TRAFFIC = {}
+# HBM bytes per launch from two rocprofv3 counter passes over `bench.py --quick`
+# (profiles/prefill_score_kernel_fp8_n131072.md): FETCH_SIZE and WRITE_SIZE in
+# KiB per dispatch, each scaled by what the same counter reads for the 1 GiB
+# calibration copy of the same run; valid while the kernel's sources hash the same
+TRAFFIC = {
+    ("prefill_score_kernel", "fp8_n131072"): {
+        "fetch_kib": 1703040, "write_kib": 3199963,
+        "copy_fetch_kib": 524301, "copy_write_kib": 1048576, "copy_bytes": 1073741824,
+        "sources_sha256": "3da5ba3a15e776648bd84a525e923a058643f58d32ef64e6e3ced40c8759c3d9",
+    },
+}
 
 
 def sources_sha256(names):
