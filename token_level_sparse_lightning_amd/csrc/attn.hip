@@ -424,6 +424,69 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             for (int ch = 0; ch < NCP; ++ch) o[db] = mma_chunk(vb[db][ch], pf[ch], o[db]);
         }
     };
+    // bf16 pipeline pieces: a wave's partial logits of one tile (its
+    // reduction dims), and the rest of a tile once the full logits are known
+    auto logits_partial = [&](const unsigned char* ct, v4f& acc0, v4f& acc1) {
+        uint4 ca[NCQ], cb[NCQ];
+#pragma unroll
+        for (int ch = 0; ch < NCQ; ++ch) {
+            ca[ch] = *reinterpret_cast<const uint4*>(ct + qoff[ch]);
+            cb[ch] = *reinterpret_cast<const uint4*>(ct + qoff[ch] + 4 * CSTR);
+        }
+        acc0 = v4f{0.f, 0.f, 0.f, 0.f};
+        acc1 = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ch = 0; ch < NCQ; ++ch) {
+            acc0 = mma_chunk(ca[ch], qf[ch], acc0);
+            acc1 = mma_chunk(cb[ch], qf[ch], acc1);
+        }
+    };
+    auto finish_tile = [&](int tcur, const unsigned char* ct, const v4f& acc0, const v4f& acc1) {
+        const int* sl = slots + tcur * AT_TS;
+        float z[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            z[r] = sl[8 * g + r] >= 0 ? acc0[r] * a.scale_log2 : -INFINITY;
+            z[4 + r] = sl[8 * g + 4 + r] >= 0 ? acc1[r] * a.scale_log2 : -INFINITY;
+        }
+        uint4 vb[NDB];
+        if constexpr (EB == 2) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const unsigned char* tp = ct + poff[db & 7] + 256 * (db >> 3);
+                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)tp);
+                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tp + 4 * CSTR));
+                const uint2 x = __builtin_bit_cast(uint2, lo), y = __builtin_bit_cast(uint2, hi);
+                vb[db] = make_uint4(x.x, x.y, y.x, y.y);
+            }
+        }
+        float mx = z[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, z[j]);
+        mx = xor32_max(xor16_max(mx));
+        const bool grow = mx > m_run + 8.f;
+        if (__ballot(grow)) {
+            const float m_new = grow ? mx : m_run;
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+            l_run *= alpha;
+            m_run = m_new;
+        }
+        const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+        float p[8];
+        float ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[j] = __builtin_amdgcn_exp2f(z[j] - m_ref);
+            ps += p[j];
+        }
+        l_run += ps;
+        const uint4 pf = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                    pack_bf16x2(p[6], p[7]));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = mma_chunk(vb[db], pf, o[db]);
+    };
     auto none = [] {};
     if constexpr (NBUF == 1) {
         // one buffer: compute, then store the next tile
@@ -503,18 +566,46 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
                 __builtin_amdgcn_s_waitcnt(0xF70);      // vmcnt(0)
             }
             __syncthreads();
-            int cur = 0, nxt = 2;
+            // Software-pipelined tiles: interval ti (between two barriers) takes
+            // the partner's partial logits of tile ti, issues tile ti+1's logit
+            // fragment reads and products, and then runs tile ti's softmax and
+            // P.V while those products are on the matrix cores; it ends by
+            // publishing tile ti+1's partial logits.  Tile ti+2 is gathered
+            // during interval ti into the buffer tile ti-1 left (its last
+            // reads, the V^T of tile ti-1, came before this interval's first
+            // barrier) and has landed by the barrier that closes it.
+            v4f a0, a1;  // this wave's partial logits of the current tile
+            logits_partial(ctile[0], a0, a1);
+            zx0[0][tid] = make_float4(a0[0], a0[1], a0[2], a0[3]);
+            zx1[0][tid] = make_float4(a1[0], a1[1], a1[2], a1[3]);
+            __builtin_amdgcn_s_waitcnt(0xF70);  // tile 1 landed
+            __syncthreads();
+            int cur = 0;
             for (int ti = 0; ti < ntl; ++ti) {
-                const bool more = ti + 2 < ntl;
-                if (more) fetch_pos(tlist[ti + 2]);
-                compute(tlist[ti], ctile[cur], ti & 1,
-                        [&] { __builtin_amdgcn_s_waitcnt(0xF70); },  // vmcnt(0): tile ti+1 landed
-                        [&] {
-                            if (more) issue_dma(nxt);
-                        },
-                        none);
-                cur = cur == 2 ? 0 : cur + 1;
-                nxt = nxt == 2 ? 0 : nxt + 1;
+                const int par = ti & 1;
+                const bool more1 = ti + 1 < ntl, more2 = ti + 2 < ntl;
+                const int nx1 = cur == 2 ? 0 : cur + 1, nx2 = nx1 == 2 ? 0 : nx1 + 1;
+                if (more2) {
+                    fetch_pos(tlist[ti + 2]);
+                    issue_dma(nx2);
+                }
+                const float4 q0 = zx0[par][tid ^ 64], q1 = zx1[par][tid ^ 64];
+                // tile ti+1: partial logits (independent of tile ti's softmax)
+                v4f n0 = {0.f, 0.f, 0.f, 0.f}, n1 = {0.f, 0.f, 0.f, 0.f};
+                if (more1) logits_partial(ctile[nx1], n0, n1);
+                __builtin_amdgcn_sched_barrier(0);
+                a0[0] += q0.x; a0[1] += q0.y; a0[2] += q0.z; a0[3] += q0.w;
+                a1[0] += q1.x; a1[1] += q1.y; a1[2] += q1.z; a1[3] += q1.w;
+                finish_tile(tlist[ti], ctile[cur], a0, a1);
+                if (more1) {
+                    zx0[par ^ 1][tid] = make_float4(n0[0], n0[1], n0[2], n0[3]);
+                    zx1[par ^ 1][tid] = make_float4(n1[0], n1[1], n1[2], n1[3]);
+                }
+                a0 = n0;
+                a1 = n1;
+                __builtin_amdgcn_s_waitcnt(0xF70);  // tile ti+2 landed
+                __syncthreads();
+                cur = nx1;
             }
         }
     }
