@@ -177,6 +177,59 @@ def test_index_prefill_sample_miss_fallback():
     np.testing.assert_array_equal(Ss[0], Ss_o)
 
 
+def _fp8_integer_inputs(n, HI, DI, seed):
+    """fp8 inputs that are small integers (exact in e4m3) at unit scales, with
+    weights in quarters: every product, sum and linear-part split on either
+    side is exact in fp32, so selections and scores must match bit for bit."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randint(-12, 13, (1, n, HI, DI), generator=g).float()
+    k = torch.randint(-12, 13, (1, n, DI), generator=g).float()
+    w = (torch.randint(-4, 5, (1, n, HI), generator=g).float() * 0.25).contiguous()
+    q8 = q.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    k8 = k.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    return q8, torch.ones(1, n), k8, torch.ones(1, n), w
+
+
+@pytest.mark.parametrize("HI", [8, 24, 40])
+def test_index_prefill_fp8_integer_exact(HI):
+    """fp8 prefill with one, two and four head blocks (24 and 40 leave masked
+    heads in the last block): bit-exact against the oracle, ties included."""
+    n, DI, k = 1200, 128, 96
+    q8, qs, k8, ks, w = _fp8_integer_inputs(n, HI, DI, 70 + HI)
+    announce(f"index_prefill fp8 integer HI={HI}")
+    S, Ss = tl.index_prefill(to_dev(q8), to_dev(k8), to_dev(w), k, q_scale=to_dev(qs), k_scale=to_dev(ks),
+                             want_scores=True)
+    torch.cuda.synchronize()
+    rows = np.arange(n)
+    S_o, Ss_o, _, _ = oracle.index_prefill_rows(FP8, host(q8), host(qs), host(k8), host(ks), host(w), k, rows)
+    np.testing.assert_array_equal(S[0].cpu().numpy(), S_o)
+    np.testing.assert_array_equal(Ss[0].cpu().numpy(), Ss_o)
+
+
+def test_prefill_decode_consistency_two_head_blocks():
+    """As below with H^I = 24 (two head blocks, eight masked heads): the
+    prefill row t equals the decode scan + top-k at length t+1 bit for bit,
+    for rows in both linear-part slots (even and odd t)."""
+    n, HI, DI, k = 1300, 24, 128, 200
+    inp = synth.indexer_prefill(1, n, HI, DI, FP8, seed=17, planted=True)
+    announce("prefill/decode consistency HI=24")
+    S, Ss = _prefill_gpu(inp, k)
+    ts = [0, 1, 199, 200, 777, 1298, 1299]
+    qd = torch.stack([inp.q[0, t] for t in ts])
+    qs = torch.stack([inp.q_scale[0, t] for t in ts])
+    wd = torch.stack([inp.w[0, t] for t in ts])
+    kc = torch.cat([inp.k[0, : t + 1] for t in ts])
+    ksc = torch.cat([inp.k_scale[0, : t + 1] for t in ts])
+    cu = torch.tensor(np.concatenate([[0], np.cumsum([t + 1 for t in ts])]), dtype=torch.int64)
+    sc = tl.index_decode(to_dev(qd), to_dev(kc), to_dev(wd), to_dev(cu), n, q_scale=to_dev(qs),
+                         k_scale=to_dev(ksc))
+    lens = torch.tensor([t + 1 for t in ts], dtype=torch.int32)
+    Sd, Ssd = tl.topk_select(sc, to_dev(cu[:-1]), to_dev(lens), k, n, want_scores=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(Sd.cpu().numpy(), S[0, ts])
+    np.testing.assert_array_equal(Ssd.cpu().numpy(), Ss[0, ts])
+
+
 def test_prefill_decode_consistency():
     """Prefill row t equals index_decode + topk_select at length t+1, bit for bit."""
     n, HI, DI, k = 1500, 64, 128, 256
