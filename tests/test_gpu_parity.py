@@ -133,7 +133,7 @@ def test_index_prefill_lowp(dt, n, k):
     for t in range(n):
         msg = parity.check_structure(S[t], t, k)
         assert msg is None, (t, msg)
-    rows = sample_rows(n, k, 40, seed=dt, extra=[255, 767, 768, 4351, 4352, 8447, 8448])
+    rows = sample_rows(n, k, 40, seed=dt, extra=[255, 767, 768, 4351, 4352, 5375, 5376, 8447, 8448])
     S_o, _, sc, mg = _oracle_rows(inp, k, rows)
     rep = parity.check_selection(S[rows], S_o, rows, k, sc)
     assert rep.ok(), rep.summary()
