@@ -53,7 +53,18 @@ __global__ __launch_bounds__(DG_NT) void selection_quality_kernel(const float* t
         ks = lo;
     }
     double tot = 0.0, cov = 0.0;
-    for (int s = tid; s < L; s += DG_NT) tot += (double)a[s];
+    {
+        // eight loads per thread in flight, added in a fixed order
+        int s = tid;
+        for (; s + 7 * DG_NT < L; s += 8 * DG_NT) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = a[s + u * DG_NT];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) tot += (double)v[u];
+        }
+        for (; s < L; s += DG_NT) tot += (double)a[s];
+    }
     for (int i = tid; i < ks; i += DG_NT) {
         const int s = Sr[i];
         if (s < L) cov += (double)a[s];

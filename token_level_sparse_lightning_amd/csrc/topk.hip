@@ -49,26 +49,6 @@ struct TopkArgs {
     float* Ss;
 };
 
-// Exclusive scan of an int over the workgroup; scratch >= NT/64 + 1 ints.
-template <int NT>
-__device__ __forceinline__ int block_excl_scan(int v, int* total, int* scratch) {
-    constexpr int NW = NT / 64;
-    const int w = threadIdx.x >> 6, l = lane_id();
-    const int incl = wave_incl_scan(v);
-    if (l == 63) scratch[w] = incl;
-    __syncthreads();
-    int base = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        const int c = scratch[i];
-        if (i < w) base += c;
-        tot += c;
-    }
-    __syncthreads();
-    *total = tot;
-    return base + incl - v;
-}
-
 __device__ __forceinline__ int sample_stride(int L) { return max(16, (L + TT_SAMPLE_MAX - 1) / TT_SAMPLE_MAX); }
 
 __global__ __launch_bounds__(TT_NT) void topk_threshold_kernel(TopkArgs a) {

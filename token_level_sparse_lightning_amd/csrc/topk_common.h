@@ -7,14 +7,8 @@
 
 namespace tlsl {
 
-constexpr int TK_LCAP = 8192;  // candidate keys gathered into LDS once a bin is this small
-
-struct TopkSmem {
-    uint32_t hist[2048];
-    uint32_t lkeys[TK_LCAP];
-    int scratch[64];
-    int lcnt;
-};
+constexpr int TK_LCAP = 8192;          // candidate keys gathered into LDS once a bin is this small
+constexpr int TK_BITMAP_WORDS = 4096;  // rows up to 131072 positions use the bitmap path
 
 // Radix digits of the 32-bit score key, most significant first.
 __device__ __forceinline__ int radix_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
@@ -30,11 +24,12 @@ __device__ __forceinline__ uint32_t radix_mask(int p) { return p == 2 ? 0x3ffu :
 // One histogram pass over the keys' own span [lo, hi] (2048 bins of 2^s keys)
 // finds the bin holding the result; the few keys of that bin are then ranked
 // against each other.  A bin with more than SEL_BLMAX keys (a span dominated
-// by near-equal keys) falls back to three radix passes over the full key.
-// exact = false stops after the histogram and returns the bin's lower edge, a
-// lower bound of the need-th largest key (*gt is then not set); the bound is
-// loose when the span is wide (2048 bins over keys of both signs).
-// Ends with a barrier, so `sm` may be reused right away.
+// by near-equal keys) becomes the range of a further level, tightened to its
+// keys' min and max (at most three more levels; a bin of equal keys ends at
+// once).  exact = false stops after the first histogram and returns the bin's
+// lower edge, a lower bound of the need-th largest key (*gt is then not set);
+// the bound is loose when the span is wide (2048 bins over keys of both
+// signs).  Ends with a barrier, so `sm` may be reused right away.
 // ---------------------------------------------------------------------------
 constexpr int SEL_BLMAX = 256;
 
@@ -46,6 +41,44 @@ struct SelectSmem {
     uint32_t tsh;
 };
 
+// Shared memory of block_topk_row: the radix path's histogram and LDS key
+// copy, or the bitmap path's select state and position bitmap.
+struct TopkSmem {
+    union {
+        struct {
+            uint32_t hist[2048];
+            uint32_t lkeys[TK_LCAP];
+            int scratch[64];
+            int lcnt;
+        } r;
+        struct {
+            SelectSmem sel;
+            uint32_t bitmap[TK_BITMAP_WORDS];
+            int nties;
+        } b;
+    };
+};
+
+// Exclusive scan of an int over the workgroup; scratch >= NT/64 + 1 ints.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* total, int* scratch) {
+    constexpr int NW = NT / 64;
+    const int w = threadIdx.x >> 6, l = lane_id();
+    const int incl = wave_incl_scan(v);
+    if (l == 63) scratch[w] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int c = scratch[i];
+        if (i < w) base += c;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + incl - v;
+}
+
 template <int NT, class Each>
 __device__ uint32_t block_select_each(int need, Each each, SelectSmem& sm, int* gt_out, bool exact) {
     const int tid = threadIdx.x;
@@ -55,67 +88,89 @@ __device__ uint32_t block_select_each(int need, Each each, SelectSmem& sm, int* 
         hi = max(hi, k);
     });
     block_minmax_u32<NT>(&lo, &hi, sm.scratch);
-    const uint32_t span = hi - lo;
-    const int s = span < 2048u ? 0 : (32 - __clz(span)) - 11;
-    for (int i = tid; i < 2048; i += NT) sm.hist[i] = 0;
-    if (tid == 0) sm.bcnt = 0;
-    __syncthreads();
-    each([&](uint32_t k) { atomicAdd(&sm.hist[(k - lo) >> s], 1u); });
-    __syncthreads();
-    int above;
-    const int d = block_find_bin<NT, 2048>(sm.hist, need, &above, sm.scratch);
-    const uint32_t edge = lo + ((uint32_t)d << s);
-    if (!exact) return edge;
-    const int nb = (int)sm.hist[d];
-    const int rank = need - above;  // inside bin d
-    __syncthreads();  // every thread holds nb before the fallback clears hist
-    uint32_t T;
-    int gt;
-    if (s == 0) {
-        T = edge;
-        gt = above;
-    } else if (nb <= SEL_BLMAX) {
-        each([&](uint32_t k) {
-            if (((k - lo) >> s) == (uint32_t)d) sm.blist[atomicAdd(&sm.bcnt, 1)] = k;
-        });
+    // Level by level: a histogram of the keys inside [lo, hi] over 2048 bins
+    // of 2^s keys finds the bin d holding the need-th largest; a bin of at
+    // most SEL_BLMAX keys is ranked directly, a larger one becomes the next
+    // level's range (tightened to its keys' own min and max, so a bin of equal
+    // keys ends the search at once).  Each level shrinks the span by 2^11.
+    int gt = 0;  // keys above the current range
+    uint32_t T = 0u;
+    for (int level = 0;; ++level) {
+        const uint32_t span = hi - lo;
+        const int s = span < 2048u ? 0 : (32 - __clz(span)) - 11;
+        for (int i = tid; i < 2048; i += NT) sm.hist[i] = 0;
+        if (tid == 0) sm.bcnt = 0;
         __syncthreads();
-        if (tid < nb) {
-            const uint32_t kj = sm.blist[tid];
-            int g = 0, e = 0;
-            for (int m = 0; m < nb; ++m) {
-                const uint32_t km = sm.blist[m];
-                g += km > kj;
-                e += km == kj;
-            }
-            if (g < rank && rank <= g + e) {  // equal keys write equal values
-                sm.tsh = kj;
-                sm.gsh = above + g;
-            }
+        {
+            // run-length counts: a thread adds a run of keys in one bin with
+            // one atomic (a bin of many equal keys would otherwise serialise
+            // every key of it on one LDS word)
+            int cur = -1;
+            uint32_t run = 0u;
+            each([&](uint32_t k) {
+                if (k >= lo && k <= hi) {
+                    const int b = (int)((k - lo) >> s);
+                    if (b != cur) {
+                        if (run) atomicAdd(&sm.hist[cur], run);
+                        cur = b;
+                        run = 0u;
+                    }
+                    ++run;
+                }
+            });
+            if (run) atomicAdd(&sm.hist[cur], run);
         }
         __syncthreads();
-        T = sm.tsh;
-        gt = sm.gsh;
-    } else {
-        uint32_t prefix = 0, pmask = 0;
-        int left = need;
-        gt = 0;
-        for (int p = 0; p < 3; ++p) {
-            const int sh = radix_shift(p);
-            const uint32_t dm = radix_mask(p);
-            for (int i = tid; i < 2048; i += NT) sm.hist[i] = 0;
-            __syncthreads();
+        int above;
+        const int d = block_find_bin<NT, 2048>(sm.hist, need, &above, sm.scratch);
+        const uint32_t edge = lo + ((uint32_t)d << s);
+        if (!exact) return edge;  // a lower bound of the need-th largest key
+        const int nb = (int)sm.hist[d];
+        const int rank = need - above;  // inside bin d
+        __syncthreads();  // every thread holds nb before hist is cleared again
+        if (s == 0) {
+            T = edge;
+            gt += above;
+            break;
+        }
+        const uint32_t bmask = ((uint32_t)1 << s) - 1u;
+        const uint32_t bhi = edge > 0xffffffffu - bmask ? 0xffffffffu : edge + bmask;  // bin d's last key
+        if (nb <= SEL_BLMAX) {
             each([&](uint32_t k) {
-                if ((k & pmask) == prefix) atomicAdd(&sm.hist[(k >> sh) & dm], 1u);
+                if (k >= edge && k <= bhi) sm.blist[atomicAdd(&sm.bcnt, 1)] = k;
             });
             __syncthreads();
-            int ab;
-            const int dd = block_find_bin<NT, 2048>(sm.hist, left, &ab, sm.scratch);
-            gt += ab;
-            left -= ab;
-            prefix |= (uint32_t)dd << sh;
-            pmask |= dm << sh;
+            if (tid < nb) {
+                const uint32_t kj = sm.blist[tid];
+                int g = 0, e = 0;
+                for (int m = 0; m < nb; ++m) {
+                    const uint32_t km = sm.blist[m];
+                    g += km > kj;
+                    e += km == kj;
+                }
+                if (g < rank && rank <= g + e) {  // equal keys write equal values
+                    sm.tsh = kj;
+                    sm.gsh = g;
+                }
+            }
+            __syncthreads();
+            T = sm.tsh;
+            gt += above + sm.gsh;
+            break;
         }
-        T = prefix;
+        // next level: the keys of bin d, between their own min and max
+        gt += above;
+        need = rank;
+        uint32_t nlo = 0xffffffffu, nhi = 0u;
+        each([&](uint32_t k) {
+            if (k >= edge && k <= bhi) {
+                nlo = min(nlo, k);
+                nhi = max(nhi, k);
+            }
+        });
+        block_minmax_u32<NT>(&nlo, &nhi, sm.scratch);
+        lo = nlo;
+        hi = nhi;
     }
     __syncthreads();
     *gt_out = gt;
@@ -220,8 +275,19 @@ __device__ void select_ordered(const uint32_t (&key)[SEG], const int (&pos)[SEG]
 template <int NT, class KeyFn>
 __device__ uint32_t block_select_adaptive(int cnt, int need, KeyFn key_of, SelectSmem& sm, int* gt_out,
                                           bool exact = true) {
+    // eight keys per thread in flight (the keys may come from global memory)
     const auto each = [&](auto&& f) {
-        for (int i = threadIdx.x; i < cnt; i += NT) {
+        int i = threadIdx.x;
+        for (; i + 7 * NT < cnt; i += 8 * NT) {
+            uint32_t kk[8];
+            bool ok[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) kk[u] = key_of(i + u * NT, &ok[u]);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (ok[u]) f(kk[u]);
+        }
+        for (; i < cnt; i += NT) {
             bool ok;
             const uint32_t k = key_of(i, &ok);
             if (ok) f(k);
@@ -235,14 +301,15 @@ __device__ uint32_t block_select_adaptive(int cnt, int need, KeyFn key_of, Selec
 // Ss (optional): each slot's score, -inf for unused slots.  All NT threads of
 // the workgroup call it; `sc` must be visible to the whole workgroup.
 //
-// Method: three radix passes over the score key (11, 11, 10 bits) find the
-// K-th largest key T and the count gt of keys above it; once the candidate
-// bin holds at most TK_LCAP keys the remaining passes run on an LDS copy.
-// A final in-order pass keeps every key > T and the first K - gt keys == T
-// (lowest positions first).
+// Radix path (rows longer than the bitmap): three radix passes over the score
+// key (11, 11, 10 bits) find the K-th largest key T and the count gt of keys
+// above it; once the candidate bin holds at most TK_LCAP keys the remaining
+// passes run on an LDS copy.  A final in-order pass keeps every key > T and
+// the first K - gt keys == T (lowest positions first).
 template <int NT>
-__device__ void block_topk_row(const float* __restrict__ sc, int L, int k, int32_t* __restrict__ S,
-                               float* __restrict__ Ss, TopkSmem& sm) {
+__device__ void block_topk_row_radix(const float* __restrict__ sc, int L, int k, int32_t* __restrict__ S,
+                                     float* __restrict__ Ss, TopkSmem& smu) {
+    auto& sm = smu.r;
     const int tid = threadIdx.x;
     const int K = min(k, L);
     if (L <= k) {
@@ -317,6 +384,86 @@ __device__ void block_topk_row(const float* __restrict__ sc, int L, int k, int32
         S[i] = -1;
         if (Ss) Ss[i] = -INFINITY;
     }
+}
+
+
+// Bitmap path (rows of at most TK_BITMAP_WORDS * 32 positions): the K-th
+// largest key T by the span select over the row's own key range (a few bins
+// of near-equal keys instead of the radix passes' crowded top digits); when
+// more keys tie at T than slots remain, the lowest positions among them by a
+// second select over inverted positions; every kept position sets its bit in
+// a position bitmap, and a prefix popcount over the bitmap gives each its
+// slot, in ascending position order.
+template <int NT>
+__device__ void block_topk_row(const float* __restrict__ sc, int L, int k, int32_t* __restrict__ S,
+                               float* __restrict__ Ss, TopkSmem& smu) {
+    const int tid = threadIdx.x;
+    const int K = min(k, L);
+    const int nwords = (L + 31) / 32;
+    if (L <= k || nwords > TK_BITMAP_WORDS) {
+        block_topk_row_radix<NT>(sc, L, k, S, Ss, smu);
+        return;
+    }
+    auto& sm = smu.b;
+    for (int i = tid; i < nwords; i += NT) sm.bitmap[i] = 0u;
+    if (tid == 0) sm.nties = 0;
+    __syncthreads();
+    int gt;
+    const uint32_t T = block_select_adaptive<NT>(
+        L, K, [&](int i, bool* ok) { *ok = true; return score_key(sc[i]); }, sm.sel, &gt);
+    const int need_ties = K - gt;
+    // row visits with eight loads per thread in flight
+    const auto visit = [&](auto&& f) {
+        int i = tid;
+        for (; i + 7 * NT < L; i += 8 * NT) {
+            uint32_t kk[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) kk[u] = score_key(sc[i + u * NT]);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) f(i + u * NT, kk[u]);
+        }
+        for (; i < L; i += NT) f(i, score_key(sc[i]));
+    };
+    int nt_local = 0;
+    visit([&](int, uint32_t key) { nt_local += key == T; });
+    nt_local = wave_sum(nt_local);
+    if (lane_id() == 0 && nt_local) atomicAdd(&sm.nties, nt_local);
+    __syncthreads();
+    // ties at T: keep the need_ties lowest positions, i.e. the largest
+    // inverted positions; when every tie is kept no selection is needed
+    uint32_t inv_cut = 0u;
+    if (sm.nties > need_ties) {
+        int tgt;
+        inv_cut = block_select_adaptive<NT>(
+            L, need_ties, [&](int i, bool* ok) { *ok = score_key(sc[i]) == T; return ~(uint32_t)i; }, sm.sel, &tgt);
+    }
+    visit([&](int i, uint32_t key) {
+        if (key > T || (key == T && ~(uint32_t)i >= inv_cut)) atomicOr(&sm.bitmap[i >> 5], 1u << (i & 31));
+    });
+    __syncthreads();
+    // ordered output: each thread owns a contiguous run of bitmap words
+    const int per = (nwords + NT - 1) / NT;
+    const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
+    int mine = 0;
+    for (int wd = w0; wd < w1; ++wd) mine += __popc(sm.bitmap[wd]);
+    int total;
+    int o = block_excl_scan<NT>(mine, &total, sm.sel.scratch);
+    for (int wd = w0; wd < w1; ++wd) {
+        uint32_t bits = sm.bitmap[wd];
+        while (bits) {
+            const int b = __builtin_ctz(bits);
+            bits &= bits - 1;
+            const int p = wd * 32 + b;
+            S[o] = p;
+            if (Ss) Ss[o] = sc[p];
+            ++o;
+        }
+    }
+    for (int i = K + tid; i < k; i += NT) {
+        S[i] = -1;
+        if (Ss) Ss[i] = -INFINITY;
+    }
+    __syncthreads();  // the caller may reuse the shared memory right away
 }
 
 }  // namespace tlsl
