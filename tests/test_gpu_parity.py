@@ -415,6 +415,38 @@ def test_sparse_attn_decode(dt, H, Dqk, Dv):
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
 
 
+def test_sparse_attn_decode_entries_beyond_4gib():
+    """A sequence whose latent entries span more than 4 GiB (3.8M entries of
+    1152 bytes, its last 64 selected): its gathers take full 64-bit addresses
+    instead of 32-bit offsets from the sequence's first entry, which the short
+    sequence before it uses.  Checked against eq.(3) over the selected entries,
+    gathered in slot order."""
+    lengths = [5000, 3_800_000]
+    H, Dqk, Dv, k = 128, 576, 512, 2048
+    q, kv = synth.attn_decode(lengths, H, Dqk, BF16, seed=18, device=DEV)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    rng = np.random.default_rng(2)
+    S = np.zeros((2, k), np.int32)
+    S[0] = np.sort(rng.choice(lengths[0], size=k, replace=False))
+    low = np.unique(rng.integers(0, lengths[1] - 64, size=4 * k))
+    low = rng.permutation(low)[: k - 64]
+    S[1] = np.sort(np.concatenate([low, np.arange(lengths[1] - 64, lengths[1])]))
+    scale = 1.0 / math.sqrt(Dqk)
+    announce("sparse_attn_decode, a sequence beyond 4 GiB of entries")
+    out, lse = tl.sparse_attn_decode(q, kv, torch.from_numpy(cu).to(DEV), torch.from_numpy(S).to(DEV), scale, Dv,
+                                     want_lse=True)
+    torch.cuda.synchronize()
+    sel = torch.from_numpy(np.concatenate([cu[b] + S[b] for b in range(2)])).to(DEV)
+    kv_sel = kv.index_select(0, sel)
+    del kv
+    torch.cuda.empty_cache()
+    S_sel = np.arange(2 * k, dtype=np.int32).reshape(2, k)
+    ref, ref_lse = oracle.sparse_attn_rows(BF16, host(q), host(kv_sel), S_sel, np.full(2, 2 * k - 1), scale, Dv)
+    err = np.abs(out.float().cpu().numpy() - ref).max()
+    assert err <= parity.ATTN_ATOL_BF16, err
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
+
+
 # ---------------------------------------------------------------------------
 # the DSA page's worked example (section 1.1, eq.(4)-(6)) on the GPU
 # ---------------------------------------------------------------------------

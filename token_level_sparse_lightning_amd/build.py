@@ -37,10 +37,13 @@ HIPCC_FLAGS = [
 # per-source flags: the calibration loop keeps its loop-carried accumulators in
 # VGPRs (the AGPR form makes the compiler rotate them through copies); the
 # indexer is scheduled for instruction-level parallelism (measured 2% faster on
-# the fp8 prefill scoring kernel, neutral elsewhere)
+# the fp8 prefill scoring kernel, neutral elsewhere); the attention kernels
+# take no decision on NaN (only on infinities), and without NaN semantics the
+# compiler drops the quieting instructions around each per-head max
 SOURCE_FLAGS = {"measure.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                 "indexer.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
-                "rerank.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+                "rerank.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+                "attn.hip": ["-fno-honor-nans"]}
 
 
 def _hipcc() -> str:

@@ -105,9 +105,10 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     // fp32 values are also kept transposed ([d][slot]) for the P.V product;
     // bf16 values are read transposed from ctile by the LDS transpose load
     __shared__ __align__(16) unsigned char vt[EB == 2 ? 16 : DV * VSTR];
-    __shared__ __align__(16) int slots[AT_KMAX];  // the row's slot range: position or -1
-    __shared__ int tile_any[AT_KMAX / AT_TS];
-    __shared__ int tlist[AT_KMAX / AT_TS];
+    __shared__ __align__(16) int slots[AT_KMAX];  // the row's slot range: entry gathered (0 if invalid)
+    __shared__ uint32_t tile_mask[AT_KMAX / AT_TS];  // by tile
+    __shared__ int tlist[AT_KMAX / AT_TS];           // listed tiles (at least one valid slot)
+    __shared__ uint32_t lmask[AT_KMAX / AT_TS];      // their masks
     __shared__ int ntl_sh;
     // partial logits of each wave, lane-contiguous (conflict-free exchange);
     // bf16: one set per tile parity (one barrier per tile separates a set's
@@ -156,22 +157,37 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     // no S (dense prefill): slot i is position i
     const int32_t* Srow = a.S ? a.S + (size_t)qrow * a.k : nullptr;
 
-    // the row's slot range, staged once: valid position or -1, padded to whole
-    // tiles; tiles without a valid slot are skipped
-    for (int i = tid; i < ntiles * AT_TS; i += NT) {
+    // the row's slot range, staged once: the entry each slot gathers, padded
+    // to whole tiles, with a validity mask per tile (bit j: slot j); each wave covers
+    // 64 consecutive slots, i.e. two tiles, per ballot
+    for (int base = 64 * w; base < ntiles * AT_TS; base += NT) {
+        const int i = base + l;
         const int pos = i < nsl ? (Srow ? Srow[sbeg + i] : sbeg + i) : -1;
-        slots[i] = (pos >= 0 && pos <= limit) ? pos : -1;
+        const bool v = pos >= 0 && pos <= limit;
+        // an invalid slot gathers the sequence's entry 0 (in bounds); its
+        // logit is masked to -inf
+        if (i < ntiles * AT_TS) slots[i] = v ? pos : 0;
+        const uint64_t vb = ballot(v);
+        if (l == 0) {
+            tile_mask[base / AT_TS] = (uint32_t)vb;
+            if (base / AT_TS + 1 < ntiles) tile_mask[base / AT_TS + 1] = (uint32_t)(vb >> 32);
+        }
     }
-    for (int i = tid; i < ntiles; i += NT) tile_any[i] = 0;
     __syncthreads();
-    for (int i = tid; i < ntiles * AT_TS; i += NT)
-        if (slots[i] >= 0) tile_any[i / AT_TS] = 1;
-    __syncthreads();
-    if (tid == 0) {
+    // tiles without a valid slot are skipped: list the others in order, with
+    // their masks
+    if (w == 0) {
         int m = 0;
-        for (int i = 0; i < ntiles; ++i)
-            if (tile_any[i]) tlist[m++] = i;
-        ntl_sh = m;
+        for (int b = 0; b < ntiles; b += 64) {
+            const uint32_t mk = b + l < ntiles ? tile_mask[b + l] : 0u;
+            const uint64_t any = ballot(mk != 0u);
+            if (mk != 0u) {
+                tlist[m + rank_below(any)] = b + l;
+                lmask[m + rank_below(any)] = mk;
+            }
+            m += __popcll(any);
+        }
+        if (l == 0) ntl_sh = m;
     }
 
     // query fragment (B operand of Z^T = C Q^T): column = head h, this wave's
@@ -246,13 +262,13 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             for (int u = 0; u < 4; ++u) {
                 // an invalid slot reads the row's entry 0 (always in bounds):
                 // its logit is masked to -inf, so its probability is exactly 0
-                const uint32_t pos = (uint32_t)max(qs[u], 0);
+                const uint32_t pos = (uint32_t)qs[u];
                 P.v[j][u] = *reinterpret_cast<const v4u*>(vsrc[j] + (size_t)pos * CROW);
             }
         }
 #pragma unroll
         for (int j = 0; j < RPER; ++j) {
-            const uint32_t pos = (uint32_t)max(sl[rrow[j]], 0);
+            const uint32_t pos = (uint32_t)sl[rrow[j]];
             P.r[j] = *reinterpret_cast<const v4u*>(rsrc[j] + (size_t)pos * CROW);
         }
     };
@@ -316,8 +332,8 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     // fragments are read and before the P.V products; `pre` and `post` run
     // just before and just after the barrier of the logit exchange (bf16: the
     // gather's wait and its next issue)
-    auto compute = [&](int tcur, const unsigned char* ct, int par, auto&& pre, auto&& post, auto&& mid) {
-        const int* sl = slots + tcur * AT_TS;
+    auto compute = [&](uint32_t tm, const unsigned char* ct, int par, auto&& pre, auto&& post, auto&& mid) {
+        const uint32_t tmg = tm >> (8 * g);  // validity of this lane's slots 8g..8g+7
 
         // ---- logits: Z^T[slot][head]; lane (g,c) gets slots 8g..8g+7 of head c
         float z[8];
@@ -351,8 +367,8 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                z[r] = sl[8 * g + r] >= 0 ? acc0[r] * a.scale_log2 : -INFINITY;
-                z[4 + r] = sl[8 * g + 4 + r] >= 0 ? acc1[r] * a.scale_log2 : -INFINITY;
+                z[r] = (tmg >> r) & 1u ? acc0[r] * a.scale_log2 : -INFINITY;
+                z[4 + r] = (tmg >> (4 + r)) & 1u ? acc1[r] * a.scale_log2 : -INFINITY;
             }
         }
         // V^T fragments of the tile, read before the softmax so that their
@@ -441,13 +457,20 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             acc1 = mma_chunk(cb[ch], qf[ch], acc1);
         }
     };
-    auto finish_tile = [&](int tcur, const unsigned char* ct, const v4f& acc0, const v4f& acc1) {
-        const int* sl = slots + tcur * AT_TS;
+    auto finish_tile = [&](uint32_t tm, const unsigned char* ct, const v4f& acc0, const v4f& acc1) {
+        // unscaled logits: the scale (positive) is applied inside the
+        // exponent, and the maximum commutes with it; invalid slots -inf
+        // (wave-uniform test: only partial tiles have any)
         float z[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            z[r] = sl[8 * g + r] >= 0 ? acc0[r] * a.scale_log2 : -INFINITY;
-            z[4 + r] = sl[8 * g + 4 + r] >= 0 ? acc1[r] * a.scale_log2 : -INFINITY;
+            z[r] = acc0[r];
+            z[4 + r] = acc1[r];
+        }
+        if (tm != 0xffffffffu) {
+            const uint32_t tmg = tm >> (8 * g);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) z[j] = (tmg >> j) & 1u ? z[j] : -INFINITY;
         }
         uint4 vb[NDB];
         if constexpr (EB == 2) {
@@ -463,7 +486,7 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
         float mx = z[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mx = fmaxf(mx, z[j]);
-        mx = xor32_max(xor16_max(mx));
+        mx = xor32_max(xor16_max(mx)) * a.scale_log2;
         const bool grow = mx > m_run + 8.f;
         if (__ballot(grow)) {
             const float m_new = grow ? mx : m_run;
@@ -473,14 +496,13 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             l_run *= alpha;
             m_run = m_new;
         }
-        const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+        const float nref = m_run == -INFINITY ? 0.f : -m_run;
         float p[8];
-        float ps = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            p[j] = __builtin_amdgcn_exp2f(z[j] - m_ref);
-            ps += p[j];
-        }
+        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(z[j], a.scale_log2, nref));  // <= 2^8; -inf gives 0
+        float ps = p[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) ps += p[j];
         l_run += ps;
         const uint4 pf = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                                     pack_bf16x2(p[6], p[7]));
@@ -499,7 +521,7 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
         for (int ti = 0; ti < ntl; ++ti) {
             load_tile(tlist[min(ti + 1, ntl - 1)], P);
             asm volatile("" ::: "memory");
-            compute(tlist[ti], ctile[0], 0, none, none, none);
+            compute(lmask[ti], ctile[0], 0, none, none, none);
             __syncthreads();
             if (ti + 1 >= ntl) break;
             store_tile(P, ctile[0]);
@@ -532,23 +554,43 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             doff[i] = 16 * (kk < 64 ? ((kk & ~15) | ((kk ^ f) & 15)) : (64 | ((kk ^ (f >> 1)) & 7)));
         }
         const uint32_t ct_lds = (uint32_t)(uintptr_t)(lds_uc*)&ctile[0][0];
+        // the entries of this thread's gather rows, read one interval before
+        // the gather is issued
         int dpos[5];
         auto fetch_pos = [&](int t) {
             const int* sl = slots + t * AT_TS;
 #pragma unroll
-            for (int i = 0; i < 5; ++i) dpos[i] = max(sl[drow[i]], 0);
+            for (int i = 0; i < 5; ++i) dpos[i] = sl[drow[i]];
         };
+        // Addresses: the sequence's first entry in a scalar base register and
+        // a 32-bit byte offset (one 24-bit multiply-add) when its entries
+        // span less than 4 GiB (wave-uniform; up to 3.7M entries of 1152
+        // bytes), else full 64-bit addresses.
+        const bool off32 = (int64_t)(limit + 1) * CROW <= (int64_t)0xFFFFFFFF;
         auto issue_dma = [&](int buf) {
             const uint32_t B = ct_lds + buf * CTB;
+            if (off32) {
 #pragma unroll
-            for (int i = 0; i < 5; ++i) {
-                if (i == 4 && nblk < 5) break;
-                const uint64_t a64 = (uint64_t)(uintptr_t)(kvrow + (size_t)dpos[i] * CROW + doff[i]);
-                const uint32_t m0v = B + 1024 * (w + 8 * i);
-                asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                             :
-                             : "s"(m0v), "v"(a64)
-                             : "memory");
+                for (int i = 0; i < 5; ++i) {
+                    if (i == 4 && nblk < 5) break;
+                    const uint32_t vo = __umul24((uint32_t)dpos[i], (uint32_t)CROW) + (uint32_t)doff[i];
+                    const uint32_t m0v = B + 1024 * (w + 8 * i);
+                    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                                 :
+                                 : "s"(m0v), "v"(vo), "s"(kvrow)
+                                 : "memory");
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 5; ++i) {
+                    if (i == 4 && nblk < 5) break;
+                    const uint64_t a64 = (uint64_t)(uintptr_t)(kvrow + (size_t)dpos[i] * CROW + doff[i]);
+                    const uint32_t m0v = B + 1024 * (w + 8 * i);
+                    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                                 :
+                                 : "s"(m0v), "v"(a64)
+                                 : "memory");
+                }
             }
         };
         if (ntl > 0) {
@@ -573,7 +615,12 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             // publishing tile ti+1's partial logits.  Tile ti+2 is gathered
             // during interval ti into the buffer tile ti-1 left (its last
             // reads, the V^T of tile ti-1, came before this interval's first
-            // barrier) and has landed by the barrier that closes it.
+            // barrier) and has landed by the barrier that closes it.  The
+            // positions of a gather are read one interval earlier, and the
+            // list entry of the tile after it one more interval ahead, so that
+            // no LDS round trip precedes the gather's issue.
+            if (ntl > 2) fetch_pos(tlist[2]);
+            int tl3 = tlist[min(3, ntl - 1)];
             v4f a0, a1;  // this wave's partial logits of the current tile
             logits_partial(ctile[0], a0, a1);
             zx0[0][tid] = make_float4(a0[0], a0[1], a0[2], a0[3]);
@@ -583,24 +630,25 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             int cur = 0;
             for (int ti = 0; ti < ntl; ++ti) {
                 const int par = ti & 1;
-                const bool more1 = ti + 1 < ntl, more2 = ti + 2 < ntl;
+                const bool more2 = ti + 2 < ntl;
                 const int nx1 = cur == 2 ? 0 : cur + 1, nx2 = nx1 == 2 ? 0 : nx1 + 1;
-                if (more2) {
-                    fetch_pos(tlist[ti + 2]);
-                    issue_dma(nx2);
-                }
+                if (more2) issue_dma(nx2);
+                const uint32_t tm = lmask[ti];
                 const float4 q0 = zx0[par][tid ^ 64], q1 = zx1[par][tid ^ 64];
+                // positions of tile ti+3 (past the end: the last tile's, unused),
+                // read ahead of the fragments so that their waits cover them
+                fetch_pos(tl3);
+                tl3 = tlist[min(ti + 4, ntl - 1)];
                 // tile ti+1: partial logits (independent of tile ti's softmax)
-                v4f n0 = {0.f, 0.f, 0.f, 0.f}, n1 = {0.f, 0.f, 0.f, 0.f};
-                if (more1) logits_partial(ctile[nx1], n0, n1);
+                // (after the last tile: products over a stale buffer, unused)
+                v4f n0, n1;
+                logits_partial(ctile[nx1], n0, n1);
                 __builtin_amdgcn_sched_barrier(0);
                 a0[0] += q0.x; a0[1] += q0.y; a0[2] += q0.z; a0[3] += q0.w;
                 a1[0] += q1.x; a1[1] += q1.y; a1[2] += q1.z; a1[3] += q1.w;
-                finish_tile(tlist[ti], ctile[cur], a0, a1);
-                if (more1) {
-                    zx0[par ^ 1][tid] = make_float4(n0[0], n0[1], n0[2], n0[3]);
-                    zx1[par ^ 1][tid] = make_float4(n1[0], n1[1], n1[2], n1[3]);
-                }
+                finish_tile(tm, ctile[cur], a0, a1);
+                zx0[par ^ 1][tid] = make_float4(n0[0], n0[1], n0[2], n0[3]);
+                zx1[par ^ 1][tid] = make_float4(n1[0], n1[1], n1[2], n1[3]);
                 a0 = n0;
                 a1 = n1;
                 __builtin_amdgcn_s_waitcnt(0xF70);  // tile ti+2 landed
