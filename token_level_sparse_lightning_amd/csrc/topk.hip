@@ -180,8 +180,10 @@ __global__ __launch_bounds__(TFIN_NT) void topk_final_kernel(TopkArgs a) {
     if (tid == 0) s.nties = 0;
     __syncthreads();
     int gt;
-    const uint32_t T = block_select_adaptive<TFIN_NT>(cnt, K, [&](int i, bool* ok) { *ok = true; return s.keys[i]; },
-                                                      s.sel, &gt);
+    // the filtered candidates (a row whose ties overflow them takes the
+    // full-row path above): one atomic per key
+    const uint32_t T = block_select_adaptive<TFIN_NT, false>(
+        cnt, K, [&](int i, bool* ok) { *ok = true; return s.keys[i]; }, s.sel, &gt);
     // ties at T: keep the (K - gt) lowest positions, i.e. the largest inverted
     // positions; when every tie is kept no selection is needed
     const int need_ties = K - gt;
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(TFIN_NT) void topk_final_kernel(TopkArgs a) {
     uint32_t inv_cut = 0u;
     if (s.nties > need_ties) {
         int tgt;
-        inv_cut = block_select_adaptive<TFIN_NT>(
+        inv_cut = block_select_adaptive<TFIN_NT, false>(
             cnt, need_ties, [&](int i, bool* ok) { *ok = s.keys[i] == T; return ~s.pos[i]; }, s.sel, &tgt);
     }
     for (int i = tid; i < cnt; i += TFIN_NT) {

@@ -79,7 +79,10 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, int* scratch) 
     return base + incl - v;
 }
 
-template <int NT, class Each>
+// RUNS: count a run of keys falling in one bin with one atomic (for key sets
+// with long runs of equal keys, e.g. a row of ties); otherwise one atomic per
+// key, with no per-key branch.
+template <int NT, bool RUNS = true, class Each>
 __device__ uint32_t block_select_each(int need, Each each, SelectSmem& sm, int* gt_out, bool exact) {
     const int tid = threadIdx.x;
     uint32_t lo = 0xffffffffu, hi = 0u;
@@ -101,7 +104,14 @@ __device__ uint32_t block_select_each(int need, Each each, SelectSmem& sm, int* 
         for (int i = tid; i < 2048; i += NT) sm.hist[i] = 0;
         if (tid == 0) sm.bcnt = 0;
         __syncthreads();
-        {
+        if (!RUNS && level == 0) {
+            // every key lies in [lo, hi]
+            each([&](uint32_t k) { atomicAdd(&sm.hist[(k - lo) >> s], 1u); });
+        } else if (!RUNS) {
+            each([&](uint32_t k) {
+                if (k >= lo && k <= hi) atomicAdd(&sm.hist[(k - lo) >> s], 1u);
+            });
+        } else {
             // run-length counts: a thread adds a run of keys in one bin with
             // one atomic (a bin of many equal keys would otherwise serialise
             // every key of it on one LDS word)
@@ -209,7 +219,7 @@ __device__ void select_ordered(const uint32_t (&key)[SEG], const int (&pos)[SEG]
             for (int u = 0; u < SEG; ++u)
                 if (tid + u * NT < cnt) f(key[u]);
         };
-        T = block_select_each<NT>(K, each, sel, &gt, true);
+        T = block_select_each<NT, false>(K, each, sel, &gt, true);
     }
     const int need_ties = K - gt;
 #pragma unroll
@@ -272,7 +282,7 @@ __device__ void select_ordered(const uint32_t (&key)[SEG], const int (&pos)[SEG]
 
 // Keys in workgroup-visible memory: key_of(i, &valid) for i < cnt, read by
 // thread i % NT.
-template <int NT, class KeyFn>
+template <int NT, bool RUNS = true, class KeyFn>
 __device__ uint32_t block_select_adaptive(int cnt, int need, KeyFn key_of, SelectSmem& sm, int* gt_out,
                                           bool exact = true) {
     // eight keys per thread in flight (the keys may come from global memory)
@@ -293,7 +303,7 @@ __device__ uint32_t block_select_adaptive(int cnt, int need, KeyFn key_of, Selec
             if (ok) f(k);
         }
     };
-    return block_select_each<NT>(need, each, sm, gt_out, exact);
+    return block_select_each<NT, RUNS>(need, each, sm, gt_out, exact);
 }
 
 // Exact selection of the K = min(k, L) best of sc[0..L) ordered by (score desc,
