@@ -26,6 +26,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "tlsl_device.h"
 #include "tlsl_internal.h"
@@ -628,8 +629,11 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             __builtin_amdgcn_s_waitcnt(0xF70);  // tile 1 landed
             __syncthreads();
             int cur = 0;
-            for (int ti = 0; ti < ntl; ++ti) {
-                const int par = ti & 1;
+            // one interval; the exchange parity is a compile-time constant (the
+            // loop runs two intervals per iteration), so the exchange addresses
+            // are immediate offsets and the partial logits need no copies
+            auto interval = [&](int ti, auto parc, v4f& c0, v4f& c1, v4f& n0, v4f& n1) {
+                constexpr int par = decltype(parc)::value;
                 const bool more2 = ti + 2 < ntl;
                 const int nx1 = cur == 2 ? 0 : cur + 1, nx2 = nx1 == 2 ? 0 : nx1 + 1;
                 if (more2) issue_dma(nx2);
@@ -641,19 +645,22 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
                 tl3 = tlist[min(ti + 4, ntl - 1)];
                 // tile ti+1: partial logits (independent of tile ti's softmax)
                 // (after the last tile: products over a stale buffer, unused)
-                v4f n0, n1;
                 logits_partial(ctile[nx1], n0, n1);
                 __builtin_amdgcn_sched_barrier(0);
-                a0[0] += q0.x; a0[1] += q0.y; a0[2] += q0.z; a0[3] += q0.w;
-                a1[0] += q1.x; a1[1] += q1.y; a1[2] += q1.z; a1[3] += q1.w;
-                finish_tile(tm, ctile[cur], a0, a1);
+                c0[0] += q0.x; c0[1] += q0.y; c0[2] += q0.z; c0[3] += q0.w;
+                c1[0] += q1.x; c1[1] += q1.y; c1[2] += q1.z; c1[3] += q1.w;
+                finish_tile(tm, ctile[cur], c0, c1);
                 zx0[par ^ 1][tid] = make_float4(n0[0], n0[1], n0[2], n0[3]);
                 zx1[par ^ 1][tid] = make_float4(n1[0], n1[1], n1[2], n1[3]);
-                a0 = n0;
-                a1 = n1;
                 __builtin_amdgcn_s_waitcnt(0xF70);  // tile ti+2 landed
                 __syncthreads();
                 cur = nx1;
+            };
+            v4f b0, b1;  // partial logits of the odd tiles
+            for (int ti = 0; ti < ntl; ti += 2) {
+                interval(ti, std::integral_constant<int, 0>{}, a0, a1, b0, b1);
+                if (ti + 1 >= ntl) break;
+                interval(ti + 1, std::integral_constant<int, 1>{}, b0, b1, a0, a1);
             }
         }
     }
