@@ -531,7 +531,7 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
     } else {
         // bf16: the tile's 36 KB go from global memory into LDS by the direct
         // global->LDS load, 1 KB (64 lanes x 16 bytes) per instruction, M0 the
-        // block's LDS address; wave w loads blocks w, w+8, ... < 36.  Lane l
+        // block's LDS address; wave w loads blocks w, w+NW, ... < 36.  Lane l
         // of block b fills tile byte 1024b + 16l, i.e. row r = (64b + l)/72,
         // stored chunk (64b + l) % 72, whose source is the entry's chunk
         // under the inverse swizzle (the XOR is its own inverse).  The loads
@@ -544,11 +544,12 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
         // landed by the barrier of tile k+1.  An invalid slot reads entry 0 of
         // the row's sequence (in bounds); its logit is masked to -inf.
         constexpr int NBLK = AT_TS * CROW / 1024;  // 36
-        const int nblk = (NBLK - w + 7) / 8;       // 5 or 4
-        int drow[5], doff[5];
+        constexpr int DPW = (NBLK + NW - 1) / NW;  // blocks per wave: 5 (8 waves), 9 (4 waves)
+        const int nblk = (NBLK - w + NW - 1) / NW;  // DPW or DPW - 1
+        int drow[DPW], doff[DPW];
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            const int p = min(64 * (w + 8 * i) + l, AT_TS * (CROW / 16) - 1);
+        for (int i = 0; i < DPW; ++i) {
+            const int p = min(64 * (w + NW * i) + l, AT_TS * (CROW / 16) - 1);
             const int r = p / (CROW / 16), kk = p % (CROW / 16);
             const int f = ((r >> 3) << 2) | (r & 3);
             drow[i] = r;
@@ -557,11 +558,11 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
         const uint32_t ct_lds = (uint32_t)(uintptr_t)(lds_uc*)&ctile[0][0];
         // the entries of this thread's gather rows, read one interval before
         // the gather is issued
-        int dpos[5];
+        int dpos[DPW];
         auto fetch_pos = [&](int t) {
             const int* sl = slots + t * AT_TS;
 #pragma unroll
-            for (int i = 0; i < 5; ++i) dpos[i] = sl[drow[i]];
+            for (int i = 0; i < DPW; ++i) dpos[i] = sl[drow[i]];
         };
         // Addresses: the sequence's first entry in a scalar base register and
         // a 32-bit byte offset (one 24-bit multiply-add) when its entries
@@ -572,10 +573,10 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             const uint32_t B = ct_lds + buf * CTB;
             if (off32) {
 #pragma unroll
-                for (int i = 0; i < 5; ++i) {
-                    if (i == 4 && nblk < 5) break;
+                for (int i = 0; i < DPW; ++i) {
+                    if (i == DPW - 1 && nblk < DPW) break;
                     const uint32_t vo = __umul24((uint32_t)dpos[i], (uint32_t)CROW) + (uint32_t)doff[i];
-                    const uint32_t m0v = B + 1024 * (w + 8 * i);
+                    const uint32_t m0v = B + 1024 * (w + NW * i);
                     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                                  :
                                  : "s"(m0v), "v"(vo), "s"(kvrow)
@@ -583,10 +584,10 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
                 }
             } else {
 #pragma unroll
-                for (int i = 0; i < 5; ++i) {
-                    if (i == 4 && nblk < 5) break;
+                for (int i = 0; i < DPW; ++i) {
+                    if (i == DPW - 1 && nblk < DPW) break;
                     const uint64_t a64 = (uint64_t)(uintptr_t)(kvrow + (size_t)dpos[i] * CROW + doff[i]);
-                    const uint32_t m0v = B + 1024 * (w + 8 * i);
+                    const uint32_t m0v = B + 1024 * (w + NW * i);
                     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                                  :
                                  : "s"(m0v), "v"(a64)
@@ -600,11 +601,12 @@ __global__ __launch_bounds__(HBW * DSPLIT * 64) void sparse_attn_kernel(AttnArgs
             if (ntl > 1) {
                 fetch_pos(tlist[1]);
                 issue_dma(1);
-                // tile 0 landed; tile 1 (this wave's last 5 or 4 loads) may be in flight
-                if (nblk == 5)
-                    __builtin_amdgcn_s_waitcnt(0xF75);  // vmcnt(5)
+                // tile 0 landed; tile 1 (this wave's last DPW or DPW - 1
+                // loads) may be in flight
+                if (nblk == DPW)
+                    __builtin_amdgcn_s_waitcnt(0xF70 | DPW);  // vmcnt(DPW)
                 else
-                    __builtin_amdgcn_s_waitcnt(0xF74);  // vmcnt(4)
+                    __builtin_amdgcn_s_waitcnt(0xF70 | (DPW - 1));
             } else {
                 __builtin_amdgcn_s_waitcnt(0xF70);      // vmcnt(0)
             }
