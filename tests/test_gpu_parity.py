@@ -392,7 +392,7 @@ def test_short_prefill_path_equals_selected_path():
     assert torch.equal(l_s, l_d)
 
 
-@pytest.mark.parametrize("dt,H,Dqk,Dv", [(BF16, 128, 576, 512), (F32, 4, 80, 64)])
+@pytest.mark.parametrize("dt,H,Dqk,Dv", [(BF16, 128, 576, 512), (BF16, 100, 576, 512), (F32, 4, 80, 64)])
 def test_sparse_attn_decode(dt, H, Dqk, Dv):
     lengths = [1, 0, 5, 64, 2048, 3000, 5000]  # an empty sequence: zero output, lse -inf
     k = 2048
