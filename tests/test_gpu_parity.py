@@ -304,6 +304,26 @@ def test_sparse_attn_prefill(dt, H, Dqk, Dv, n, k):
     np.testing.assert_allclose(lse.cpu().numpy()[0][rows], ref_lse, rtol=1e-4, atol=1e-4)
 
 
+def test_sparse_attn_prefill_batch_of_two():
+    """Two batch rows: each row's slots index its own sequence's entries
+    (entry b*n + s), with holes, out-of-range and duplicate slots."""
+    B, n, H, k = 2, 260, 128, 96
+    q, kv = synth.attn_prefill(B, n, H, 576, BF16, seed=19)
+    S = np.stack([_random_selection(n, k, seed=20 + b, messy=True) for b in range(B)])
+    scale = 1.0 / math.sqrt(576)
+    announce("sparse_attn_prefill B=2")
+    out, lse = tl.sparse_attn_prefill(to_dev(q), to_dev(kv), torch.from_numpy(S).to(DEV), scale, 512,
+                                      want_lse=True)
+    torch.cuda.synchronize()
+    per = sample_rows(n, k, 10, seed=21, extra=(31, 32, 95, 96, 97))
+    rows = np.concatenate([b * n + per for b in range(B)])
+    ref, ref_lse = oracle.sparse_attn_prefill_rows(BF16, host(q), host(kv), S, scale, rows, 512)
+    got = out.float().cpu().numpy().reshape(B * n, H, 512)[rows]
+    err = np.abs(got - ref).max()
+    assert err <= parity.ATTN_ATOL_BF16, err
+    np.testing.assert_allclose(lse.cpu().numpy().reshape(B * n, H)[rows], ref_lse, rtol=1e-4, atol=1e-4)
+
+
 def test_sparse_attn_prefill_tile_pipeline():
     # many tiles per row (every rotation of the tile buffers), whole tiles
     # without a valid slot in the middle of a row, a ragged last tile (k=300)
@@ -412,6 +432,34 @@ def test_sparse_attn_decode(dt, H, Dqk, Dv):
     tol = parity.ATTN_ATOL_F32 if dt == F32 else parity.ATTN_ATOL_BF16
     err = np.abs(out.float().cpu().numpy() - ref).max()
     assert err <= tol, err
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
+
+
+def test_sparse_attn_decode_messy_slots():
+    """Decode selections with holes (-1), positions at or past the sequence's
+    length (skipped), duplicates (counted twice) and a whole 32-slot tile
+    without a valid slot."""
+    lengths = [700, 3000, 40, 2500]
+    H, k = 128, 1024
+    q, kv = synth.attn_decode(lengths, H, 576, BF16, seed=22)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    rng = np.random.default_rng(23)
+    S = np.full((len(lengths), k), -1, np.int32)
+    for b, L in enumerate(lengths):
+        K = min(k, L)
+        S[b, :K] = np.sort(rng.choice(L, size=K, replace=False))
+        S[b, 5] = -1                 # hole
+        S[b, 7] = L + 3              # past the sequence: skipped
+        S[b, 9] = S[b, 8]            # duplicate
+        S[b, 64:96] = -1             # a tile with no valid slot
+    scale = 1.0 / math.sqrt(576)
+    announce("sparse_attn_decode messy slots")
+    out, lse = tl.sparse_attn_decode(to_dev(q), to_dev(kv), torch.from_numpy(cu).to(DEV),
+                                     torch.from_numpy(S).to(DEV), scale, 512, want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.sparse_attn_decode(BF16, host(q), host(kv), cu, S, scale, 512)
+    err = np.abs(out.float().cpu().numpy() - ref).max()
+    assert err <= parity.ATTN_ATOL_BF16, err
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4, atol=1e-4)
 
 
