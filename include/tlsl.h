@@ -212,7 +212,7 @@ int topk_select_noalloc(const float* scores, const int64_t* row_start, const int
  *   qI [B,n,HI,dI] bf16, kI [B,n,dI] bf16, wI [B,n,HI] fp32,
  *   S [B,n,k] int32, p [B,n,k] fp32; outputs fp32.
  * Supported: dt = BF16 with dI = 128, 1 <= HI <= 64, 1 <= k <= 4096,
- * B*n <= 2^30.  Scores, softmax and products accumulate in fp32 (the
+ * n < 2^22, B*n <= 2^30 (else TLSL_ERR_UNSUPPORTED / TLSL_ERR_SHAPE).  Scores, softmax and products accumulate in fp32 (the
  * coefficients of the backward products carry ~16 significant bits).  loss,
  * dq and dw are bitwise reproducible; dk is accumulated with atomic adds, so
  * its last bits may vary between runs.  Needs no workspace.

@@ -186,6 +186,29 @@ def test_attention_validation():
     assert g(P, P, P, P, 64, 128, 576, 512, 4097, 0.04, 1, P, None, None, ctypes.byref(size), None) == ERR_UNSUP
 
 
+def test_indexer_loss_grad_validation():
+    lib = _lib()
+    f = lib.indexer_loss_grad
+    args = lambda **kw: dict(dict(q=P, k=P, w=P, S=P, p=P, B=1, n=64, HI=64, dI=128, topk=16, dt=1,
+                                  loss=P, dq=P, dk=P, dw=P), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return f(a["q"], a["k"], a["w"], a["S"], a["p"], a["B"], a["n"], a["HI"], a["dI"], a["topk"], a["dt"],
+                 a["loss"], a["dq"], a["dk"], a["dw"], None)
+
+    assert call(p=None) == ERR_NULL
+    assert call(dk=None) == ERR_NULL
+    assert call(n=0) == ERR_SHAPE
+    assert call(B=1 << 10, n=(1 << 20) + 1) == ERR_SHAPE            # B*n above 2^30
+    assert call(dt=2) == ERR_UNSUP
+    assert call(dI=64) == ERR_UNSUP
+    assert call(HI=65) == ERR_UNSUP
+    assert call(topk=4097) == ERR_UNSUP
+    assert call(n=1 << 22) == ERR_UNSUP                             # dK rows take 32-bit byte offsets
+    assert call(dq=MIS) == ERR_ALIGN
+
+
 def test_binding_refuses_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))

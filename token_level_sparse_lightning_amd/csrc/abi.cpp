@@ -207,6 +207,8 @@ int indexer_loss_grad(const void* qI, const void* kI, const float* wI, const int
     if (dt != TLSL_BF16 || dI != 128 || HI > 64 || k > 4096)
         return fail(TLSL_ERR_UNSUPPORTED, "indexer_loss_grad: (dtype %s, HI=%d, dI=%d, k=%d) not built "
                     "(bf16, dI 128, HI 1..64, k 1..4096)", dt_name(dt), HI, dI, k);
+    if (n >= (1 << 22))  // one sequence's dK rows are addressed with 32-bit byte offsets below 2^31
+        return fail(TLSL_ERR_UNSUPPORTED, "indexer_loss_grad: n=%d above the supported 4194303", n);
     if (!aligned16(qI) || !aligned16(kI) || !aligned16(wI) || !aligned16(S) || !aligned16(p) || !aligned16(loss) ||
         !aligned16(dq) || !aligned16(dk) || !aligned16(dw))
         return fail(TLSL_ERR_ALIGN, "indexer_loss_grad: pointers not 16-byte aligned");

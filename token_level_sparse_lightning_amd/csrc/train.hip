@@ -5,10 +5,12 @@
 // its gradient into the indexer's inputs q^I, k^I and w^I (the inputs are
 // detached from the main model, so the gradient stops there).
 //
-// One workgroup (four waves) per query row t:
+// One workgroup (four waves) per query row t; the row's slot positions are
+// staged in LDS first, so no global load waits behind the dK additions:
 //  1. the selected keys' scores I_i = sum_j w_j ReLU(q_j . k_{S_i}) are
 //     recomputed with the indexer's scoring tile (bit-identical to the
-//     prefill's S_score), 64 gathered keys per wave step, into LDS;
+//     prefill's S_score), 64 gathered keys per wave step (the next step's
+//     keys in flight), into LDS;
 //  2. softmax over the valid slots, the teacher normalised by its mass on
 //     them, the row's loss and g_i = Softmax(I)_i - P_i;
 //  3. per 64-slot tile (keys gathered into LDS), wave w owns head block w:
@@ -17,7 +19,8 @@
 //       dQ^T += K^T A^T (dims x heads; K^T read with the LDS transpose load),
 //     then, after the four waves have put A^T in LDS, wave w owns dims
 //     32w..32w+31 of D = A^T Q (keys x dims), read back transposed, and adds D
-//     to the gathered keys' rows of dK.
+//     to the gathered keys' rows of dK; the next tile's keys are loaded into
+//     registers meanwhile.
 // A^T enters the products split into two bf16 terms (high part and
 // remainder), so the coefficients carry ~16 significant bits and the
 // gradients keep fp32-level accuracy.  dK rows collect contributions from
@@ -36,7 +39,6 @@ namespace tlsl {
 
 constexpr int TR_NT = 256;                 // four waves
 constexpr int TR_DI = 128;                 // indexer dims (bf16)
-constexpr int TR_KMAX = 4096;              // slots per row
 constexpr int TR_KROW = TR_DI * 2 + 32;    // LDS row of a gathered key (bytes, padded)
 constexpr int TR_QROW = TR_DI * 2 + 32;    // LDS row of one query head
 constexpr int TR_AROW = 64 * 2 + 16;       // LDS row of A^T transposed: 64 keys of one head
@@ -115,7 +117,9 @@ __global__ __launch_bounds__(TR_NT, 2) void indexer_kl_kernel(TrainArgs a) {
     __shared__ __align__(16) unsigned char qt[64 * TR_QROW];     // the row's query, heads padded to 64
     __shared__ __align__(16) unsigned char kt[64 * TR_KROW];     // the tile's gathered keys
     __shared__ __align__(16) unsigned char at[2][64 * TR_AROW];  // A^T split, stored [head][key]
-    __shared__ __align__(16) float gb[TR_KMAX];                  // scores, then g
+    // dynamic: the slots' scores, then g (float[64 nsub]); the slots' positions
+    // (int[64 nsub], -1 where the slot is invalid or outside [0, t])
+    extern __shared__ __align__(16) unsigned char trdyn[];
     __shared__ float red[8];
 
     const int tid = threadIdx.x, l = lane_id(), g = l >> 4, c = l & 15;
@@ -128,38 +132,53 @@ __global__ __launch_bounds__(TR_NT, 2) void indexer_kl_kernel(TrainArgs a) {
     const int32_t* Srow = a.S + (size_t)row * K;
     const float* prow = a.p + (size_t)row * K;
     const unsigned char* kbase = a.k + tok0 * (DI * 2);
+    float* gb = reinterpret_cast<float*>(trdyn);
+    int* spl = reinterpret_cast<int*>(trdyn + (size_t)nsub * 64 * 4);
 
-    // ---- the query into LDS (heads >= HI are zero rows) ----------------------
+    // ---- the query and the row's positions into LDS ---------------------------
     for (int i = tid; i < 64 * (DI * 2 / 16); i += TR_NT) {
         const int h = i / (DI * 2 / 16), ch = i % (DI * 2 / 16);
         uint4 v = make_uint4(0, 0, 0, 0);
         if (h < a.HI) v = *reinterpret_cast<const uint4*>(a.q + ((size_t)row * a.HI + h) * (DI * 2) + ch * 16);
         *reinterpret_cast<uint4*>(qt + h * TR_QROW + ch * 16) = v;
     }
+    for (int i = tid; i < nsub * 64; i += TR_NT) {
+        const int sp = i < K ? Srow[i] : -1;
+        spl[i] = (sp >= 0 && sp <= t) ? sp : -1;
+    }
+    __syncthreads();
 
     // ---- 1. scores of the selected keys -------------------------------------
+    // Each wave scores subtiles wv, wv + 4, ...; the next subtile's keys are
+    // loaded while the current one is scored.
     {
         uint4 qf[4][NCH];
         float wvv[4][4];
         I::load_query(a.q + (size_t)row * a.HI * (DI * 2), a.w + (size_t)row * a.HI, 1.f, a.HI, true, qf, wvv);
-        for (int j = wv; j < nsub; j += 4) {
-            // lane (g, c) of key block kb holds key 16kb + c of the subtile
-            uint4 kf[4][NCH];
-            int pos[4];
+        // lane (g, c) of key block kb holds key 16kb + c of the subtile
+        auto load_sub = [&](int j, uint4(&kf)[4][NCH]) {
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const int slot = 64 * j + 16 * kb + c;
-                const int sp = slot < K ? Srow[slot] : -1;
-                pos[kb] = (sp >= 0 && sp <= t) ? sp : 0;
-                const uint4* src = reinterpret_cast<const uint4*>(kbase + (size_t)pos[kb] * (DI * 2) + g * (DI * 2 / 4));
+                const int sp = spl[64 * j + 16 * kb + c];
+                const uint4* src =
+                    reinterpret_cast<const uint4*>(kbase + (size_t)(sp >= 0 ? sp : 0) * (DI * 2) + g * (DI * 2 / 4));
 #pragma unroll
                 for (int ch = 0; ch < NCH; ++ch) kf[kb][ch] = src[ch];
             }
-            const float sc = I::score(qf, wvv, kf);
-            const int slot = 64 * j + l;
-            if (slot < K) {
-                const int sp = Srow[slot];
-                gb[slot] = (sp >= 0 && sp <= t) ? sc : -INFINITY;
+        };
+        if (wv < nsub) {
+            uint4 kf[4][NCH];
+            load_sub(wv, kf);
+            for (int j = wv; j < nsub; j += 4) {
+                uint4 kn[4][NCH];
+                load_sub(min(j + 4, nsub - 1), kn);  // past the end: a repeat, unused
+                const float sc = I::score(qf, wvv, kf);
+                const int slot = 64 * j + l;
+                if (slot < K) gb[slot] = spl[slot] >= 0 ? sc : -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int ch = 0; ch < NCH; ++ch) kf[kb][ch] = kn[kb][ch];
             }
         }
     }
@@ -215,19 +234,41 @@ __global__ __launch_bounds__(TR_NT, 2) void indexer_kl_kernel(TrainArgs a) {
 #pragma unroll
     for (int db = 0; db < 8; ++db) dqa[db] = v4f{0.f, 0.f, 0.f, 0.f};
     float dwa = 0.f;
-    // per-thread gather item of a tile: key row tid/4, 64 bytes at (tid%4)*64
+    // Gather item of a thread: key row tid/4 of the tile, 64 bytes at
+    // (tid%4)*64.  Tile j+1 is loaded into registers while tile j is
+    // computed and stored into the tile buffer once every wave is done with
+    // tile j; its loads are issued before tile j's dK additions, so waiting
+    // for them does not wait for those.
     const int grow = tid >> 2, gq = tid & 3;
-    for (int j = 0; j < nsub && live; ++j) {
-        {
-            const int slot = 64 * j + grow;
-            const int sp = slot < K ? Srow[slot] : -1;
-            const bool ok = sp >= 0 && sp <= t;
-            const uint4* src = reinterpret_cast<const uint4*>(kbase + (size_t)(ok ? sp : 0) * (DI * 2) + gq * 64);
-            uint4* dst = reinterpret_cast<uint4*>(kt + grow * TR_KROW + gq * 64);
+    uint4 pf[4];
+    auto gather_load = [&](int j) {
+        const int sp = spl[64 * j + grow];
+        const uint4* src = reinterpret_cast<const uint4*>(kbase + (size_t)(sp >= 0 ? sp : 0) * (DI * 2) + gq * 64);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) dst[u] = ok ? src[u] : make_uint4(0, 0, 0, 0);
-        }
+        for (int u = 0; u < 4; ++u) pf[u] = src[u];
+    };
+    auto gather_store = [&](int j) {
+        const bool ok = spl[64 * j + grow] >= 0;
+        uint4* dst = reinterpret_cast<uint4*>(kt + grow * TR_KROW + gq * 64);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dst[u] = ok ? pf[u] : make_uint4(0, 0, 0, 0);
+    };
+    // dK rows of this sequence as a buffer resource: an invalid slot's
+    // additions get an offset past the end, and the hardware drops them, so
+    // the additions are issued unconditionally (a fixed count of memory
+    // operations per tile).  n * DI * 4 < 2^31 (checked by the caller).
+    const __amdgpu_buffer_rsrc_t dkr = __builtin_amdgcn_make_buffer_rsrc(a.dk + tok0 * DI, 0, a.n * DI * 4, 0x00020000);
+    if (live && nsub > 0) {
+        gather_load(0);
+        gather_store(0);
         __syncthreads();
+    }
+    // nothing loaded before the loop (w of the lane's head) is left pending
+    // into it, where a wait for it would also wait for the tile in flight
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+    for (int j = 0; j < nsub && live; ++j) {
+        const bool more = j + 1 < nsub;
+        if (more) gather_load(j + 1);
         // X^T = K Q^T for this wave's head block: lane (g, c) gets keys 16kb + 4g + r, head h
         v4f x[4];
         {
@@ -308,18 +349,22 @@ __global__ __launch_bounds__(TR_NT, 2) void indexer_kl_kernel(TrainArgs a) {
         }
         // lane (g, c): keys 16kb + 4g + r, dim 32wv + 16db2 + c
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb) {
+            const int4 sp4 = *reinterpret_cast<const int4*>(spl + 64 * j + 16 * kb + 4 * g);
+            const int spv[4] = {sp4.x, sp4.y, sp4.z, sp4.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int slot = 64 * j + 16 * kb + 4 * g + r;
-                const int sp = slot < K ? Srow[slot] : -1;
-                if (sp >= 0 && sp <= t) {
-                    float* dst = a.dk + (tok0 + sp) * DI + 32 * wv + c;
+                const int off = spv[r] >= 0 ? (spv[r] * DI + 32 * wv + c) * 4 : (int)0x80000000;
 #pragma unroll
-                    for (int db2 = 0; db2 < 2; ++db2) unsafeAtomicAdd(dst + 16 * db2, da[kb][db2][r]);
-                }
+                for (int db2 = 0; db2 < 2; ++db2)
+                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(da[kb][db2][r], dkr, off + 64 * db2, 0, 0);
             }
-        __syncthreads();  // the tile and A^T are overwritten next
+        }
+        __syncthreads();  // every wave is done with the tile and A^T
+        if (more) {
+            gather_store(j + 1);
+            __syncthreads();
+        }
     }
 
     // ---- 4. dQ and dW of the row ----------------------------------------------
@@ -351,8 +396,9 @@ hipError_t launch_indexer_kl(const void* q, const void* k, const float* w, const
     const size_t nk = (size_t)B * n * TR_DI;
     const int zb = (int)std::min<size_t>((nk + TR_NT - 1) / TR_NT, (size_t)device_cu_count() * 8);
     TLSL_TIMED_LAUNCH("zero_f32_kernel", st, hipLaunchKernelGGL(zero_f32_kernel, dim3(zb), dim3(TR_NT), 0, st, dk, nk));
+    const size_t dyn = (size_t)((topk + 63) / 64) * 64 * 8;  // scores/g and positions of the row's slots
     TLSL_TIMED_LAUNCH("indexer_kl_kernel", st,
-                      hipLaunchKernelGGL(indexer_kl_kernel, dim3(B * n), dim3(TR_NT), 0, st, a));
+                      hipLaunchKernelGGL(indexer_kl_kernel, dim3(B * n), dim3(TR_NT), dyn, st, a));
     return hipGetLastError();
 }
 
