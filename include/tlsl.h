@@ -351,6 +351,23 @@ const char* tlsl_last_error(void);
 /* Library version string. */
 const char* tlsl_version(void);
 
+/*
+ * tlsl_set_debug -- device checks of the index metadata that callers pass in
+ * device memory, which the host-side validation cannot read: on (on != 0),
+ * index_decode checks cu_seqlens[0] == 0, sparse_attn_decode and
+ * index_decode that cu_seqlens is non-decreasing with every length below
+ * 2^31 - 2^12, and topk_select, topk_select_noalloc, selection_quality and
+ * cutoff_margin that every row_start >= 0 and 0 <= row_len < 2^31 - 2^12.  A
+ * violation returns TLSL_ERR_SHAPE (the message names the first offending
+ * entry and its values) and launches nothing else.  Each check is one small
+ * kernel followed by a synchronisation of the call's stream, so it is meant
+ * for finding malformed batches, not for timed runs or graph capture.  Off
+ * by default; the environment variable TLSL_DEBUG (any value but "0") turns
+ * it on at the first call.  Returns the previous state (0 or 1).  Process-wide
+ * (every thread and device).
+ */
+int tlsl_set_debug(int on);
+
 #ifdef __cplusplus
 }
 #endif

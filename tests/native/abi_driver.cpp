@@ -11,6 +11,9 @@
 #include "../../include/tlsl.h"
 
 extern int g_launches;
+namespace tlsl {
+extern int g_debug_checks;
+}
 static int g_fail = 0;
 static float sc0() { return 0.05f; }
 
@@ -155,6 +158,20 @@ int main() {
         fprintf(stderr, "expected 16 launches, saw %d\n", g_launches);
         ++g_fail;
     }
+    // the debug switch: off by default; on, the calls with device-side
+    // metadata run their device check before the launch
+    if (tlsl::g_debug_checks != 0) { fprintf(stderr, "device checks ran with the debug switch off\n"); ++g_fail; }
+    if (tlsl_set_debug(1) != 0) { fprintf(stderr, "debug switch on by default\n"); ++g_fail; }
+    size_t ws2 = 0;
+    EXPECT(index_decode(P, F, P, F, F, I64, 4, 64, 128, 1000, TLSL_FP8_E4M3, F, nullptr, &ws2, nullptr), TLSL_OK);
+    EXPECT(topk_select(F, I64, I32, 64, 2048, 131072, I32, F, nullptr, &need, nullptr), TLSL_OK);  // size query only
+    ws2 = need;
+    EXPECT(topk_select(F, I64, I32, 64, 2048, 131072, I32, F, P, &ws2, nullptr), TLSL_OK);
+    if (tlsl::g_debug_checks != 2) {
+        fprintf(stderr, "expected 2 device checks with the debug switch on, saw %d\n", tlsl::g_debug_checks);
+        ++g_fail;
+    }
+    if (tlsl_set_debug(0) != 1) { fprintf(stderr, "debug switch did not report its previous state\n"); ++g_fail; }
     if (g_fail) return 1;
     printf("abi driver ok\n");
     return 0;

@@ -70,4 +70,13 @@ hipError_t launch_sparse_attn_decode(const AttnShape&, const void*, const void*,
     ++g_launches;
     return hipErrorInvalidValue;  // the launch-error path: mapped to TLSL_ERR_HIP
 }
+int g_debug_checks = 0;
+int debug_check_seqlens(const int64_t*, int, bool, hipStream_t, const char*) {
+    ++g_debug_checks;
+    return 0;
+}
+int debug_check_rows(const int64_t*, const int32_t*, int, hipStream_t, const char*) {
+    ++g_debug_checks;
+    return 0;
+}
 }  // namespace tlsl

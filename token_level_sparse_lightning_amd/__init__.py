@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     indexer_loss_grad,
     load,
     selection_quality,
+    set_debug,
     sparse_attn_decode,
     sparse_attn_decode_workspace_bytes,
     sparse_attn_prefill,

@@ -19,7 +19,7 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 
 EXPORTS = ("index_prefill", "index_prefill_rerank", "index_decode", "topk_select", "topk_select_noalloc", "sparse_attn_prefill",
            "dense_attn_prefill", "dsa_prefill", "sparse_attn_decode", "indexer_loss_grad", "selection_quality", "cutoff_margin",
-           "tlsl_last_error", "tlsl_version",
+           "tlsl_last_error", "tlsl_version", "tlsl_set_debug",
            # measurement aids (include/tlsl_measure.h)
            "tlsl_timer_arm", "tlsl_timer_collect", "tlsl_calib_copy", "tlsl_calib_mfma")
 
@@ -62,6 +62,8 @@ def load():
         getattr(lib, fn).restype = I
     lib.tlsl_last_error.restype = ctypes.c_char_p
     lib.tlsl_version.restype = ctypes.c_char_p
+    lib.tlsl_set_debug.argtypes = [I]
+    lib.tlsl_set_debug.restype = I
     D = ctypes.POINTER(ctypes.c_double)
     lib.tlsl_timer_arm.argtypes = [ctypes.c_char_p, I]
     lib.tlsl_timer_collect.argtypes = [ctypes.POINTER(I), D, D, D]
@@ -366,6 +368,12 @@ def indexer_loss_grad(qI, kI, wI, S, p, loss=None, dq=None, dk=None, dw=None, st
 
 
 # ---- measurement aids (include/tlsl_measure.h) --------------------------------
+def set_debug(on: bool) -> bool:
+    """Switch the device checks of cu_seqlens / row_start / row_len on or off
+    (tlsl_set_debug); returns the previous state."""
+    return bool(load().tlsl_set_debug(1 if on else 0))
+
+
 def timer_arm(kernel: str, max_launches: int = 4096) -> None:
     """Bracket every following launch of ``kernel`` with HIP events on its stream."""
     lib = load()

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtlsl.so")
 
-SOURCES = ["abi.cpp", "plan.cpp", "indexer.hip", "topk.hip", "attn.hip", "train.hip", "diag.hip", "rerank.hip", "measure.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "indexer.hip", "topk.hip", "attn.hip", "train.hip", "diag.hip", "rerank.hip", "debug.hip", "measure.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

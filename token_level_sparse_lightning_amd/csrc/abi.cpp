@@ -4,7 +4,10 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <atomic>
 
 #include "../../include/tlsl.h"
 #include "tlsl_internal.h"
@@ -85,7 +88,24 @@ int check_topk(const float* scores, const int64_t* row_start, const int32_t* row
     return 0;
 }
 
+// debug switch: -1 until the environment has been read
+std::atomic<int> g_debug{-1};
+
+int debug_state() {
+    int v = g_debug.load(std::memory_order_relaxed);
+    if (v < 0) {
+        const char* e = getenv("TLSL_DEBUG");
+        const int from_env = (e && *e && strcmp(e, "0") != 0) ? 1 : 0;
+        int expected = -1;
+        g_debug.compare_exchange_strong(expected, from_env);
+        v = g_debug.load(std::memory_order_relaxed);
+    }
+    return v;
+}
+
 }  // namespace
+
+bool tlsl::debug_enabled() { return debug_state() == 1; }
 
 int tlsl::report(int code, const char* fmt, ...) {
     if (code == TLSL_OK || !fmt) {
@@ -104,6 +124,12 @@ extern "C" {
 const char* tlsl_last_error(void) { return g_err; }
 
 const char* tlsl_version(void) { return "tlsl 0.1 (gfx950)"; }
+
+int tlsl_set_debug(int on) {
+    const int prev = debug_state();
+    g_debug.store(on ? 1 : 0, std::memory_order_relaxed);
+    return prev;
+}
 
 int index_prefill(const void* qI, const float* q_scale, const void* kI, const float* k_scale, const float* wI, int B,
                   int n, int HI, int dI, int k, tlsl_dtype dt, int32_t* S, float* S_score, void* workspace,
@@ -162,6 +188,7 @@ int index_decode(const void* qI, const float* q_scale, const void* kI_cache, con
     (void)workspace;
     if (ws_bytes) *ws_bytes = 0;  // needs no workspace
     tlsl::IndexerShape s{dt, HI, dI};
+    if (tlsl::debug_enabled() && (rc = tlsl::debug_check_seqlens(cu_seqlens, B, true, stream, "index_decode"))) return rc;
     return launch_result(tlsl::launch_index_decode(s, qI, q_scale, kI_cache, k_scale, wI, cu_seqlens, B, max_len,
                                                    scores, stream),
                          "index_decode");
@@ -173,6 +200,7 @@ int topk_select(const float* scores, const int64_t* row_start, const int32_t* ro
     if (rc) return rc;
     rc = workspace_protocol(workspace, ws_bytes, tlsl::topk_ws_bytes(R, k, max_len));
     if (rc) return rc > 0 ? ok() : rc;
+    if (tlsl::debug_enabled() && (rc = tlsl::debug_check_rows(row_start, row_len, R, stream, "topk_select"))) return rc;
     return launch_result(tlsl::launch_topk_select(scores, row_start, row_len, R, k, max_len, S, S_score, workspace,
                                                   stream),
                          "topk_select");
@@ -180,7 +208,7 @@ int topk_select(const float* scores, const int64_t* row_start, const int32_t* ro
 
 int topk_select_noalloc(const float* scores, const int64_t* row_start, const int32_t* row_len, int R, int k,
                         int max_len, int32_t* S, float* S_score, hipStream_t stream) {
-    const int rc = check_topk(scores, row_start, row_len, R, k, max_len, S, S_score, "topk_select_noalloc");
+    int rc = check_topk(scores, row_start, row_len, R, k, max_len, S, S_score, "topk_select_noalloc");
     if (rc) return rc;
     const size_t need = tlsl::topk_ws_bytes(R, k, max_len);
     if (need > (size_t)TLSL_NOALLOC_SCRATCH_BYTES)
@@ -192,6 +220,9 @@ int topk_select_noalloc(const float* scores, const int64_t* row_start, const int
     const hipError_t e = tlsl::topk_noalloc_scratch(&ws);
     if (e != hipSuccess)
         return fail(TLSL_ERR_HIP, "topk_select_noalloc: device address of the scratch array: %s", hipGetErrorString(e));
+    if (tlsl::debug_enabled() &&
+        (rc = tlsl::debug_check_rows(row_start, row_len, R, stream, "topk_select_noalloc")))
+        return rc;
     return launch_result(tlsl::launch_topk_select(scores, row_start, row_len, R, k, max_len, S, S_score, ws, stream),
                          "topk_select_noalloc");
 }
@@ -226,6 +257,8 @@ int selection_quality(const float* teacher, const int64_t* row_start, const int3
     if (!aligned16(recall) || !aligned16(mass)) return fail(TLSL_ERR_ALIGN, "selection_quality: pointers not 16-byte aligned");
     rc = workspace_protocol(workspace, ws_bytes, tlsl::selection_quality_ws_bytes(R, m, max_len));
     if (rc) return rc > 0 ? ok() : rc;
+    if (tlsl::debug_enabled() && (rc = tlsl::debug_check_rows(row_start, row_len, R, stream, "selection_quality")))
+        return rc;
     return launch_result(tlsl::launch_selection_quality(teacher, row_start, row_len, R, S, k, m, max_len, recall, mass,
                                                         workspace, stream),
                          "selection_quality");
@@ -241,6 +274,8 @@ int cutoff_margin(const float* scores, const int64_t* row_start, const int32_t* 
     if (!aligned16(margin)) return fail(TLSL_ERR_ALIGN, "cutoff_margin: margin not 16-byte aligned");
     rc = workspace_protocol(workspace, ws_bytes, tlsl::cutoff_margin_ws_bytes(R, k, max_len));
     if (rc) return rc > 0 ? ok() : rc;
+    if (tlsl::debug_enabled() && (rc = tlsl::debug_check_rows(row_start, row_len, R, stream, "cutoff_margin")))
+        return rc;
     return launch_result(tlsl::launch_cutoff_margin(scores, row_start, row_len, R, k, max_len, margin, workspace, stream),
                          "cutoff_margin");
 }
@@ -351,8 +386,10 @@ int sparse_attn_decode(const void* q, const void* kv_cache, const int64_t* cu_se
     if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(S) || !aligned16(out) || !aligned16(lse) || !aligned16(cu_seqlens))
         return fail(TLSL_ERR_ALIGN, "sparse_attn_decode: pointers not 16-byte aligned");
     const size_t need = tlsl::attn_decode_ws_bytes(s, B, k);
-    const int rc = workspace_protocol(workspace, ws_bytes, need);
+    int rc = workspace_protocol(workspace, ws_bytes, need);
     if (rc) return rc > 0 ? ok() : rc;
+    if (tlsl::debug_enabled() && (rc = tlsl::debug_check_seqlens(cu_seqlens, B, false, stream, "sparse_attn_decode")))
+        return rc;
     return launch_result(tlsl::launch_sparse_attn_decode(s, q, kv_cache, cu_seqlens, S, B, k, softmax_scale, out, lse,
                                                          workspace, stream),
                          "sparse_attn_decode");

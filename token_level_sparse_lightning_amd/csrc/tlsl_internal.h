@@ -26,6 +26,17 @@ void timer_mark(const char* kernel, hipStream_t st, bool after);
         ::tlsl::timer_mark(name, st, true);     \
     } while (0)
 
+// ---- optional device checks of caller-provided index metadata ----------------
+// On while tlsl_set_debug(1) is in force or TLSL_DEBUG is set (to anything but
+// "0") in the environment at the first call.
+bool debug_enabled();
+// One check kernel on `st`, then a synchronisation of `st`; TLSL_OK, or an
+// error code with the message set.  cu_seqlens: non-decreasing, every length
+// below 2^31 - 2^12, and cu_seqlens[0] == 0 when first_zero.  Rows:
+// row_start >= 0 and 0 <= row_len < 2^31 - 2^12.
+int debug_check_seqlens(const int64_t* cu, int B, bool first_zero, hipStream_t st, const char* fn);
+int debug_check_rows(const int64_t* row_start, const int32_t* row_len, int R, hipStream_t st, const char* fn);
+
 // ---- indexer ---------------------------------------------------------------
 struct IndexerShape {
     int dt;      // 0 f32, 1 bf16, 2 fp8
