@@ -129,7 +129,13 @@ static int read_verdict(long long* d, hipStream_t st, long long (&h)[4], const c
     return TLSL_OK;
 }
 
+// One verdict array per device: checks are serialised on the host (launch,
+// copy back, synchronise) so that two threads checking at once cannot read
+// each other's verdict.
+static std::mutex g_check_mu;
+
 int debug_check_seqlens(const int64_t* cu, int B, bool first_zero, hipStream_t st, const char* fn) {
+    std::lock_guard<std::mutex> lock(g_check_mu);
     long long* d = nullptr;
     hipError_t e = verdict_addr(&d);
     if (e != hipSuccess) return report(TLSL_ERR_HIP, "%s: device check failed: %s", fn, hipGetErrorString(e));
@@ -152,6 +158,7 @@ int debug_check_seqlens(const int64_t* cu, int B, bool first_zero, hipStream_t s
 }
 
 int debug_check_rows(const int64_t* row_start, const int32_t* row_len, int R, hipStream_t st, const char* fn) {
+    std::lock_guard<std::mutex> lock(g_check_mu);
     long long* d = nullptr;
     hipError_t e = verdict_addr(&d);
     if (e != hipSuccess) return report(TLSL_ERR_HIP, "%s: device check failed: %s", fn, hipGetErrorString(e));
