@@ -510,19 +510,26 @@ def calibrate(steps):
     return res
 
 
-def cpu_baseline(inp, k, n, target_s=15.0):
+def cpu_baseline(inp, k, n, S_gpu=None, target_s=15.0):
     """Oracle pairs/s on a bounded, evenly spread sample of query rows.
 
-    A short calibration call sizes the sample to about ``target_s`` seconds."""
+    A short calibration call sizes the sample to about ``target_s`` seconds.
+    When the GPU's selection of the workload (``S_gpu`` [n, k], on the host)
+    is given, the oracle's selections of the sampled rows are compared with
+    it: the fraction of identical slots and the rows that differ (the margin
+    rule on the differing slots is the GPU tests' job: it needs every score
+    of the row)."""
     import oracle
+    from oracle import parity
     sn = synth.storage_to_numpy
     oracle.build()
     nthreads = oracle.num_threads()
     q, qs, kk, ks, w = sn(inp.q), sn(inp.q_scale), sn(inp.k), sn(inp.k_scale), sn(inp.w)
+    last = {}
 
     def run(rows):
         t0 = time.perf_counter()
-        oracle.index_prefill_rows(inp.dt, q, qs, kk, ks, w, k, rows)
+        last["S"] = oracle.index_prefill_rows(inp.dt, q, qs, kk, ks, w, k, rows)[0]
         return time.perf_counter() - t0
 
     cal = np.linspace(n // 2, n - 1, nthreads).astype(np.int64)
@@ -532,9 +539,16 @@ def cpu_baseline(inp, k, n, target_s=15.0):
     sel = np.unique(np.linspace(0, n - 1, rows_n).astype(np.int64))
     dt = run(sel)
     pairs = int((sel + 1).sum())
-    return dict(value=pairs / dt, unit="pairs/s", cores=nthreads, kind="oracle",
-                sample=f"{len(sel)} evenly spaced query rows of the headline workload "
-                       f"({pairs} causal pairs, {dt:.1f} s, double precision, OpenMP over rows)")
+    res = dict(value=pairs / dt, unit="pairs/s", cores=nthreads, kind="oracle",
+               sample=f"{len(sel)} evenly spaced query rows of the headline workload "
+                      f"({pairs} causal pairs, {dt:.1f} s, double precision, OpenMP over rows)")
+    if S_gpu is not None:
+        rep = parity.check_selection(S_gpu[sel], last["S"], sel, k)
+        res["parity"] = dict(rows=rep.rows, slots=rep.slots, match=rep.matched / max(rep.slots, 1),
+                             rows_differing=rep.mismatched_rows, structure_errors=len(rep.structure_errors))
+        log(f"parity on the sampled rows: match {res['parity']['match']:.6f}, {rep.mismatched_rows} of "
+            f"{rep.rows} rows differ, {len(rep.structure_errors)} structure errors")
+    return res
 
 
 # HBM traffic of a kernel per launch on one workload, from two rocprofv3 --pmc
@@ -604,10 +618,12 @@ def main():
 
     N_HEAD, K_HEAD, SEED_HEAD = 131072, 2048, 5
     head, inp, S = bench_prefill(N_HEAD, synth.DT_FP8, SEED_HEAD, args.steps, args.warmup, plant_max_dist=100000)
-    # the headline inputs go to the host for the CPU baseline and are freed on
-    # the device before the other workloads
+    # the headline inputs (and, for the parity statistics of the CPU baseline,
+    # its selection) go to the host and are freed on the device before the
+    # other workloads
     inp = synth.IndexerPrefill(inp.dt, inp.q.cpu(), inp.q_scale.cpu(), inp.k.cpu(), inp.k_scale.cpu(), inp.w.cpu(),
                                inp.probes)
+    S_host = None if args.no_cpu else S[0].cpu().numpy()
     torch.cuda.empty_cache()
     extra = {}
     if "attn_prefill_131072" in want:
@@ -645,7 +661,7 @@ def main():
         extra["tiny_f32_512"] = bench_tiny(args.steps, args.warmup)
         torch.cuda.empty_cache()
     calib = None if args.no_calib else calibrate(args.steps)
-    cpu = None if args.no_cpu else cpu_baseline(inp, K_HEAD, N_HEAD)
+    cpu = None if args.no_cpu else cpu_baseline(inp, K_HEAD, N_HEAD, S_gpu=S_host)
 
     roofline = {"bound": "mfma", "achieved": head["kernel_tflops"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": head["frac"],
@@ -676,6 +692,9 @@ def main():
         "headline": head,
         "calibration": calib,
         "extra": extra,
+        "library_sources_sha256": sources_sha256(sorted(
+            f for f in os.listdir(os.path.join(ROOT, "token_level_sparse_lightning_amd", "csrc"))
+            if f.endswith((".hip", ".cpp", ".h")))),
     }
     print(json.dumps(line), flush=True)
 
