@@ -261,6 +261,36 @@ def test_index_prefill_deterministic():
     np.testing.assert_array_equal(a[1], b[1])
 
 
+def test_attention_and_decode_step_deterministic():
+    """Bitwise reproducibility, promised for every call but the training
+    step's dk: the prefill attention and a whole decode step (scan, row
+    top-k, decode attention) run twice give identical bytes."""
+    n, k, H = 600, 256, 128
+    q, kv = synth.attn_prefill(1, n, H, 576, BF16, seed=13)
+    S = torch.from_numpy(_random_selection(n, k, seed=5)[None]).to(DEV)
+    announce("sparse_attn_prefill determinism")
+    runs = [tl.sparse_attn_prefill(to_dev(q), to_dev(kv), S, 1 / 24.0, 512, want_lse=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+
+    lengths = np.array([3000, 5000, 100, 0, 2049], dtype=np.int64)
+    di = synth.indexer_decode(lengths, 64, 128, FP8, seed=17, device=DEV)
+    qa, kva = synth.attn_decode(lengths, H, 576, BF16, seed=17, device=DEV)
+    row_len = torch.as_tensor(lengths, dtype=torch.int32, device=DEV)
+    announce("decode step determinism")
+    outs = []
+    for _ in range(2):
+        sc = tl.index_decode(di.q, di.k, di.w, di.cu_seqlens, int(lengths.max()), q_scale=di.q_scale,
+                             k_scale=di.k_scale)
+        Sd, Ssd = tl.topk_select(sc, di.cu_seqlens[:-1].contiguous(), row_len, 512, int(lengths.max()),
+                                 want_scores=True)
+        o, lse = tl.sparse_attn_decode(qa, kva, di.cu_seqlens, Sd, 1 / 24.0, 512, want_lse=True)
+        outs.append((sc, Sd, Ssd, o, lse))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 def test_index_prefill_without_scores():
     inp = synth.indexer_prefill(1, 1200, 64, 128, BF16, seed=9)
     announce("index_prefill S only")
