@@ -121,6 +121,7 @@ def causal_pairs(B, n):
 # ---------------------------------------------------------------------------
 def bench_prefill(n, dt, seed, steps, warmup, plant_max_dist=None):
     HI, DI, k = 64, 128, 2048
+    torch.cuda.reset_peak_memory_stats()
     log(f"prefill n={n} dt={synth.DT_NAMES[dt]}: generating inputs")
     inp = synth.indexer_prefill(1, n, HI, DI, dt, seed, planted=True, plant_max_dist=plant_max_dist,
                                 device=DEV)
@@ -159,7 +160,7 @@ def bench_prefill(n, dt, seed, steps, warmup, plant_max_dist=None):
                pairs_per_s=pairs / (tm.wall * 1e-3), pairs=pairs, flops_per_call=flops,
                call_tflops=call_tf, kernel="prefill_score_kernel", kernel_tflops=kern_tf, peak_tflops=peak,
                frac=kern_tf / peak, call_frac=call_tf / peak, algorithmic_bytes_per_call=nbytes,
-               planted_recall=recall, **tm.as_dict())
+               planted_recall=recall, peak_device_bytes=torch.cuda.max_memory_allocated(), **tm.as_dict())
     return res, inp, S
 
 
@@ -391,6 +392,7 @@ def _quality_ws_bytes(R, k, m, max_len):
 
 def bench_decode(seed, steps, warmup):
     B, HI, DI, H, Dqk, Dv, k = 64, 64, 128, 128, 576, 512, 2048
+    torch.cuda.reset_peak_memory_stats()
     lengths = synth.decode_lengths(B, 16384, 131072, seed)
     log(f"decode: sumL={int(lengths.sum())}: generating inputs")
     di = synth.indexer_decode(lengths, HI, DI, synth.DT_FP8, seed, device=DEV)
@@ -477,6 +479,7 @@ def bench_decode(seed, steps, warmup):
                          f"fp8 indexer H^I={HI} d^I={DI}, top-{k}, bf16 attention H={H} Dqk={Dqk} Dv={Dv}",
                 tokens_per_s=B / (tm.wall * 1e-3), bytes_per_step=nbytes, achieved_gbs=gbs,
                 peak_gbs=PEAK_HBM_GBS, frac=gbs / PEAK_HBM_GBS, stages=stages, planted_recall=planted_hit,
+                peak_device_bytes=torch.cuda.max_memory_allocated(),
                 diagnostics=diag,
                 **tm.as_dict())
 

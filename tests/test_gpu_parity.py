@@ -291,6 +291,31 @@ def test_attention_and_decode_step_deterministic():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("dt", [BF16, FP8])
+def test_rank_invariance_on_the_gpu(dt):
+    """DSA page, section 3.1: a positive rescaling of the scores leaves the
+    selection unchanged.  Doubling w (and, for fp8, the key scales) doubles
+    every product and sum exactly, so the GPU's S must be bit-identical and
+    S_score exactly twice the original, in prefill and decode."""
+    inp = synth.indexer_prefill(1, 3000, 64, 128, dt, seed=23, planted=True, device=DEV)
+    k = 700
+    announce(f"rank invariance dt={dt}")
+    S1, Ss1 = tl.index_prefill(inp.q, inp.k, inp.w, k, q_scale=inp.q_scale, k_scale=inp.k_scale, want_scores=True)
+    w2 = inp.w * 2
+    ks2 = inp.k_scale * 2 if inp.k_scale is not None else None
+    S2, Ss2 = tl.index_prefill(inp.q, inp.k, w2, k, q_scale=inp.q_scale, k_scale=ks2, want_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(S1, S2)
+    assert torch.equal(Ss1 * (4 if dt == FP8 else 2), Ss2)
+    lengths = np.array([2500, 40, 1800], dtype=np.int64)
+    di = synth.indexer_decode(lengths, 64, 128, dt, seed=29, device=DEV)
+    sc1 = tl.index_decode(di.q, di.k, di.w, di.cu_seqlens, 2500, q_scale=di.q_scale, k_scale=di.k_scale)
+    dks2 = di.k_scale * 2 if di.k_scale is not None else None
+    sc2 = tl.index_decode(di.q, di.k, di.w * 2, di.cu_seqlens, 2500, q_scale=di.q_scale, k_scale=dks2)
+    torch.cuda.synchronize()
+    assert torch.equal(sc1 * (4 if dt == FP8 else 2), sc2)
+
+
 def test_index_prefill_without_scores():
     inp = synth.indexer_prefill(1, 1200, 64, 128, BF16, seed=9)
     announce("index_prefill S only")
