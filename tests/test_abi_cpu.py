@@ -209,6 +209,24 @@ def test_indexer_loss_grad_validation():
     assert call(dq=MIS) == ERR_ALIGN
 
 
+def test_debug_switch(monkeypatch):
+    """tlsl_set_debug returns the previous state; the device checks it
+    switches on run only where a launch would follow (a size query returns
+    before them, so it stays valid on a host without a GPU)."""
+    lib = _lib()
+    prev = lib.tlsl_set_debug(1)
+    try:
+        assert prev in (0, 1)
+        assert lib.tlsl_set_debug(1) == 1
+        need = ctypes.c_size_t(0)
+        assert lib.topk_select(P, P, P, 64, 2048, 131072, P, None, None, ctypes.byref(need), None) == OK
+        assert need.value > 0
+        assert lib.tlsl_set_debug(0) == 1
+        assert lib.tlsl_set_debug(0) == 0
+    finally:
+        lib.tlsl_set_debug(prev)
+
+
 def test_binding_refuses_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
