@@ -4,6 +4,8 @@
 //
 // index_prefill on the fp8 inputs with budget k' gives each row's candidates
 // C_t (ascending positions, then -1).  rerank_kernel, one workgroup per row:
+//  0. the row's candidate positions are staged in LDS, so that no gather
+//     waits for a position loaded from global memory just before it;
 //  1. each wave scores 64 candidates at a time with the fine (bf16) query and
 //     the candidates' fine keys, gathered straight from global memory, through
 //     the indexer's scoring tile (idx_tile.h: the same instructions as
@@ -37,6 +39,7 @@ __global__ __launch_bounds__(RR_NT) void rerank_kernel(RerankArgs a) {
     constexpr int NCH = I::NCH;
     constexpr int SEG = CAPMAX / RR_NT;
     __shared__ float sc[CAPMAX];
+    __shared__ int cpos[CAPMAX];  // the row's candidate positions
     __shared__ SelectSmem sel;
     __shared__ int gcnt[2][SEG * (RR_NT / 64)];
     const int tid = threadIdx.x, l = lane_id(), g = l >> 4, c = l & 15;
@@ -48,6 +51,8 @@ __global__ __launch_bounds__(RR_NT) void rerank_kernel(RerankArgs a) {
     const int nc = min(a.kc, t + 1);
     const int32_t* Crow = a.C + (size_t)row * a.kc;
     const unsigned char* kbase = a.k + tok0 * I::ROWB;
+    for (int i = tid; i < nc; i += RR_NT) cpos[i] = Crow[i];
+    __syncthreads();
     {
         uint4 qf[HB][NCH];
         float wvv[HB][4];
@@ -59,7 +64,7 @@ __global__ __launch_bounds__(RR_NT) void rerank_kernel(RerankArgs a) {
             for (int kb = 0; kb < 4; ++kb) {
                 const int i = min(64 * j + 16 * kb + c, nc - 1);  // past the end: a valid, unused key
                 const uint4* src =
-                    reinterpret_cast<const uint4*>(kbase + (size_t)Crow[i] * I::ROWB + g * (I::ROWB / 4));
+                    reinterpret_cast<const uint4*>(kbase + (size_t)cpos[i] * I::ROWB + g * (I::ROWB / 4));
 #pragma unroll
                 for (int ch = 0; ch < NCH; ++ch) kf[kb][ch] = src[ch];
             }
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(RR_NT) void rerank_kernel(RerankArgs a) {
     for (int u = 0; u < SEG; ++u) {
         const int i = tid + u * RR_NT;
         key[u] = i < nc ? score_key(sc[i]) : 0u;
-        pos[u] = i < nc ? Crow[i] : -1;
+        pos[u] = i < nc ? cpos[i] : -1;
     }
     select_ordered<RR_NT, SEG>(key, pos, nc, min(a.topk, nc), a.topk, a.S + (size_t)row * a.topk,
                                a.Ss ? a.Ss + (size_t)row * a.topk : nullptr, sel, gcnt);
