@@ -631,16 +631,20 @@ def test_worked_example_attention_on_gpu():
 # index_decode batch sizes: a multiple of the scan's 256-thread prefix loop,
 # one past it, and the path for more than 4096 sequences
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("B", [256, 257, 4100])
-def test_index_decode_batch_sizes(B):
+@pytest.mark.parametrize("B,max_len", [(256, None), (257, None), (4096, None), (4096, 4_000_000), (4100, None)])
+def test_index_decode_batch_sizes(B, max_len):
+    """B = 4096 is the largest batch of the balanced scan: its LDS then holds
+    the 4097-entry subtile prefix and sequence starts (~49 KB) next to the
+    score stage; with a large max_len every wave stages its own scores in
+    what is left (the most LDS the scan takes)."""
     rng = np.random.default_rng(B)
     lengths = rng.integers(1, 300, size=B)
     lengths[B // 3] = 0          # an empty sequence
     lengths[-1] = 513            # the last sequence is the longest
     inp = synth.indexer_decode(lengths, 64, 128, FP8, seed=B, planted=False)
-    announce(f"index_decode B={B} sumL={int(lengths.sum())}")
-    sc = tl.index_decode(to_dev(inp.q), to_dev(inp.k), to_dev(inp.w), to_dev(inp.cu_seqlens), int(lengths.max()),
-                         q_scale=to_dev(inp.q_scale), k_scale=to_dev(inp.k_scale))
+    announce(f"index_decode B={B} sumL={int(lengths.sum())} max_len={max_len}")
+    sc = tl.index_decode(to_dev(inp.q), to_dev(inp.k), to_dev(inp.w), to_dev(inp.cu_seqlens),
+                         max_len or int(lengths.max()), q_scale=to_dev(inp.q_scale), k_scale=to_dev(inp.k_scale))
     torch.cuda.synchronize()
     ref, mag = oracle.index_decode(FP8, host(inp.q), host(inp.q_scale), host(inp.k), host(inp.k_scale),
                                    host(inp.w), host(inp.cu_seqlens))
